@@ -1,0 +1,191 @@
+"""ctypes binding of liblazyflash.so (C ABI in include/lazyflash.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch provides device memory (outputs and the backward workspace are
+allocated here as torch tensors) and the current HIP stream.  The library is
+loaded from this package directory; if it is missing the import of any entry
+point raises, there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block_select",
+           "attn_bwd", "bwd_workspace_bytes", "EXPORTED_SYMBOLS", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
+ABI_VERSION = 1
+LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
+LF_BF16, LF_F32 = 0, 1
+EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_bwd_workspace_bytes",
+                    "lf_status_str", "lf_last_error", "lf_abi_version")
+
+
+class LazyFlashError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class LfShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load the shared library once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LazyFlashError(-1, f"{path} is missing: build it with "
+                                 "`python -m block_sparse_backward_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, S, I32, U64, D, Z = (ctypes.c_void_p, ctypes.POINTER(LfShape), ctypes.c_int32,
+                            ctypes.c_uint64, ctypes.c_double, ctypes.c_size_t)
+    lib.lf_attn_fwd.argtypes = [S, P, P, P, P, P, P]
+    lib.lf_attn_fwd.restype = I32
+    lib.lf_block_select.argtypes = [S, P, P, D, U64, P, P, P, P, P, P, P]
+    lib.lf_block_select.restype = I32
+    lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.lf_attn_bwd.restype = I32
+    lib.lf_bwd_workspace_bytes.argtypes = [S]
+    lib.lf_bwd_workspace_bytes.restype = Z
+    lib.lf_status_str.argtypes = [I32]
+    lib.lf_status_str.restype = ctypes.c_char_p
+    lib.lf_last_error.argtypes = []
+    lib.lf_last_error.restype = ctypes.c_char_p
+    lib.lf_abi_version.argtypes = []
+    lib.lf_abi_version.restype = I32
+    if lib.lf_abi_version() != ABI_VERSION:
+        raise LazyFlashError(-1, "liblazyflash.so ABI version mismatch; rebuild it")
+    _lib = lib
+    return lib
+
+
+def _check(lib, status):
+    if status != LF_OK:
+        raise LazyFlashError(status, "%s: %s" % (lib.lf_status_str(status).decode(),
+                                                 lib.lf_last_error().decode()))
+
+
+def make_shape(B, Hq, Hkv, N, d, block, causal, scale, dtype):
+    code = {torch.bfloat16: LF_BF16, torch.float32: LF_F32}.get(dtype)
+    if code is None:
+        raise LazyFlashError(LF_EUNSUPPORTED, f"dtype {dtype} is not supported")
+    return LfShape(int(B), int(Hq), int(Hkv), int(N), int(d), int(block), int(bool(causal)),
+                   float(scale), code)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape_from(q, k, block, causal, scale):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = d ** -0.5
+    return make_shape(B, Hq, Hkv, N, d, block, causal, scale, q.dtype), scale
+
+
+def attn_fwd(q, k, v, causal=True, scale=None, block=128):
+    """Dense forward: returns (o [B,Hq,N,d] like q, lse [B,Hq,N] float32)."""
+    lib = load()
+    shp, _ = _shape_from(q, k, block, causal, scale)
+    dev = q.device
+    _need(q, "q", q.shape, q.dtype, dev)
+    _need(k, "k", (shp.batch, shp.heads_kv, shp.seqlen, shp.head_dim), q.dtype, dev)
+    _need(v, "v", k.shape, q.dtype, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    _check(lib, lib.lf_attn_fwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                _stream(dev)))
+    return o, lse
+
+
+def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads_kv=None):
+    """Masses, tau, draw and compaction.  Returns a dict of device tensors:
+    D [B,Hq,N] f32, mass [B,Hq,nqb] f64, tau [B,Hq] f64, block_w [B,Hq,nqb] f32,
+    kept_idx [B,Hq,nqb] i32, kept_count [B,Hq] i32."""
+    lib = load()
+    B, Hq, N, d = o.shape
+    shp = make_shape(B, Hq, heads_kv or Hq, N, d, block, causal,
+                     d ** -0.5 if scale is None else scale, o.dtype)
+    dev = o.device
+    _need(o, "o", o.shape, o.dtype, dev)
+    _need(dout, "dout", o.shape, o.dtype, dev)
+    nqb = N // block if block else 0
+    out = dict(
+        D=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+        mass=torch.empty((B, Hq, nqb), dtype=torch.float64, device=dev),
+        tau=torch.empty((B, Hq), dtype=torch.float64, device=dev),
+        block_w=torch.empty((B, Hq, nqb), dtype=torch.float32, device=dev),
+        kept_idx=torch.empty((B, Hq, nqb), dtype=torch.int32, device=dev),
+        kept_count=torch.empty((B, Hq), dtype=torch.int32, device=dev),
+    )
+    _check(lib, lib.lf_block_select(ctypes.byref(shp), _ptr(o), _ptr(dout), float(delta),
+                                    ctypes.c_uint64(int(seed) & (2**64 - 1)), _ptr(out["D"]),
+                                    _ptr(out["mass"]), _ptr(out["tau"]), _ptr(out["block_w"]),
+                                    _ptr(out["kept_idx"]), _ptr(out["kept_count"]), _stream(dev)))
+    return out
+
+
+def bwd_workspace_bytes(shape):
+    return int(load().lf_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, workspace=None,
+             out=None):
+    """Sparse backward over the kept blocks of `sel` (the dict of block_select).
+    Returns (dq, dk, dv).  `workspace` (uint8 device tensor) and `out`
+    (preallocated (dq, dk, dv)) are optional."""
+    lib = load()
+    shp, _ = _shape_from(q, k, block, causal, scale)
+    dev = q.device
+    B, Hq, N, d = q.shape
+    nqb = N // block
+    _need(k, "k", (B, shp.heads_kv, N, d), q.dtype, dev)
+    _need(v, "v", k.shape, q.dtype, dev)
+    _need(dout, "dout", q.shape, q.dtype, dev)
+    _need(lse, "lse", (B, Hq, N), torch.float32, dev)
+    _need(sel["D"], "D", (B, Hq, N), torch.float32, dev)
+    _need(sel["kept_idx"], "kept_idx", (B, Hq, nqb), torch.int32, dev)
+    _need(sel["kept_count"], "kept_count", (B, Hq), torch.int32, dev)
+    _need(sel["block_w"], "block_w", (B, Hq, nqb), torch.float32, dev)
+    need = int(lib.lf_bwd_workspace_bytes(ctypes.byref(shp)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _check(lib, lib.lf_attn_bwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(lse),
+                                _ptr(dout), _ptr(sel["D"]), _ptr(sel["kept_idx"]),
+                                _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                _stream(dev)))
+    return dq, dk, dv

@@ -1,0 +1,33 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lf {
+
+// A validated problem shape (see lazyflash.h for the meaning of each field).
+struct Problem {
+    int B, Hq, Hkv, N, d, block, nqb, causal;
+    float scale;
+    bool bf16;
+};
+
+hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* v, void* o,
+                      float* lse, hipStream_t st);
+
+hipError_t launch_select(const Problem& pb, const void* o, const void* dout, double delta,
+                         uint64_t seed, float* D, double* mass, double* tau, float* block_w,
+                         int32_t* kept_idx, int32_t* kept_count, hipStream_t st);
+
+hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
+                      const float* lse, const void* dout, const float* D,
+                      const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
+                      void* dq, void* dk, void* dv, float* dq_acc, hipStream_t st);
+
+// Workgroup -> work-item maps that keep every workgroup of one key/value head
+// group on one XCD (workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2), so the K/V, Q and dO tiles a group shares stay in one L2.
+constexpr int kNumXcd = 8;
+
+}  // namespace lf

@@ -1,0 +1,307 @@
+// Block selection: per-block gradient masses and the D row term (one HBM
+// streaming pass), then per (batch, head) the budget threshold tau, the Philox
+// draw, the 1/p weights and the compacted kept-block list.
+//
+// Method: the LazyFlash journal entry on gyom.fr ("LazyFlash allège la
+// rétropropagation de l'attention, 5,72 fois"), section "Un budget sur la masse
+// de gradient, et un tirage qui garde le gradient non biaisé": blocks are ranked
+// by the norm of their output gradient, a budget delta bounds the discarded
+// share of gradient mass per head and per step, blocks are kept with a
+// probability proportional to their gradient and reweighted to stay unbiased.
+//
+// Every floating-point operation that decides the kept set is done in IEEE
+// double with one rounding per operation in a fixed order (this file is
+// compiled with -ffp-contract=off), so the kept set is reproducible bit for
+// bit by any implementation of the same rule.
+#include "lf_common.h"
+#include "lf_internal.h"
+
+namespace lf {
+
+// ---------------------------------------------------------------------------
+// Kernel A: one workgroup of 256 threads per query block (b, h, i).
+// The block is the contiguous run of L = block*d elements at offset blk*L.
+// Thread t owns elements e + 8t + 2048s (e < 8, s < L/2048), loaded as one
+// 16-byte vector per s (coalesced), which lets the fp64 halving tree run as:
+// in-thread levels over s, then 8 cross-thread levels (t + 128, t + 64, ...,
+// t + 1), then 3 in-vector levels over e.
+// ---------------------------------------------------------------------------
+template <typename T, int L, int HD>
+__global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
+                                                     const T* __restrict__ dout,
+                                                     float* __restrict__ D,
+                                                     double* __restrict__ mass) {
+    constexpr int S = L / 2048;
+    constexpr int LANES_PER_ROW = HD / 8;
+    const size_t blk = blockIdx.x;
+    const int t = threadIdx.x;
+    const T* g = dout + blk * (size_t)L;
+    const T* go = o + blk * (size_t)L;
+
+    float x[S][8];
+    float y[S][8];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        load8(g + 8 * t + 2048 * s, x[s]);
+        load8(go + 8 * t + 2048 * s, y[s]);
+    }
+
+    // D: each (t, s) covers 8 columns of row (8t + 2048s) / HD.
+    constexpr int ROWS = L / HD;  // = block
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += x[s][e] * y[s][e];
+#pragma unroll
+        for (int off = LANES_PER_ROW / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        if ((t % LANES_PER_ROW) == 0) {
+            const int r = (8 * t + 2048 * s) / HD;
+            D[blk * (size_t)ROWS + r] = part;
+        }
+    }
+
+    // Mass: squares are exact in fp64; only the additions round.
+    double v[S][8];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double a = (double)x[s][e];
+            v[s][e] = __dmul_rn(a, a);
+        }
+#pragma unroll
+    for (int half = S / 2; half >= 1; half >>= 1)
+#pragma unroll
+        for (int s = 0; s < half; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[s][e] = __dadd_rn(v[s][e], v[s + half][e]);
+
+    __shared__ double red[8][256];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[e][t] = v[0][e];
+    __syncthreads();
+    if (t < 128) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[e][t] = __dadd_rn(red[e][t], red[e][t + 128]);
+    }
+    __syncthreads();
+    if (t < 64) {
+        double w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = __dadd_rn(red[e][t], red[e][t + 64]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = __dadd_rn(w[e], __shfl_down(w[e], off));
+        if (t == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = __dadd_rn(w[e], w[e + 4]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) w[e] = __dadd_rn(w[e], w[e + 2]);
+            mass[blk] = __dadd_rn(w[0], w[1]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): the round multiplies
+// words 0 and 2 by the two round constants and mixes the high halves with
+// words 1, 3 and the key; the key gains the two Weyl constants before every
+// round but the first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t philox_first_word(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                      uint64_t c3, uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += W0; k1 += W1; }
+        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    }
+    return c0;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel B: one workgroup of 1024 threads per (b, h).
+// LDS: sorted masses, running sums A and Q (3 * P doubles, P = pow2 >= nqb).
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+
+__global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
+    const double* __restrict__ mass, double delta, uint64_t seed, int Hq, int nqb, int P,
+    double* __restrict__ tau_out, float* __restrict__ block_w, int32_t* __restrict__ kept_idx,
+    int32_t* __restrict__ kept_count) {
+    extern __shared__ double smem[];
+    double* srt = smem;       // [P]
+    double* accA = smem + P;  // [P]
+    double* accQ = smem + 2 * P;
+    __shared__ int s_nonfinite, s_npos, s_kstar, s_wave[kSelThreads / 64], s_base;
+    __shared__ double s_tau;
+
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int b = bh / Hq, h = bh % Hq;
+    const double* m = mass + (size_t)bh * nqb;
+    if (tid == 0) { s_nonfinite = 0; s_npos = 0; s_kstar = 0x7fffffff; s_base = 0; }
+    __syncthreads();
+
+    int my_pos = 0, my_bad = 0;
+    for (int i = tid; i < P; i += kSelThreads) {
+        double v = __builtin_inf();
+        if (i < nqb) {
+            const double mi = m[i];
+            if (!__builtin_isfinite(mi)) my_bad = 1;
+            if (mi > 0.0) { v = mi; ++my_pos; }
+        }
+        srt[i] = v;
+    }
+    if (my_bad) atomicOr(&s_nonfinite, 1);
+    if (my_pos) atomicAdd(&s_npos, my_pos);
+    __syncthreads();
+    const bool nonfinite = s_nonfinite != 0;
+    const int n = s_npos;
+
+    if (!nonfinite && n > 0 && delta != 0.0) {
+        // bitonic sort, ascending (positives first, +inf padding last)
+        for (int k = 2; k <= P; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < P; i += kSelThreads) {
+                    const int ixj = i ^ j;
+                    if (ixj > i) {
+                        const double a = srt[i], c = srt[ixj];
+                        const bool up = (i & k) == 0;
+                        if ((a > c) == up) { srt[i] = c; srt[ixj] = a; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // sequential running sums in ascending order (one rounding per op)
+        if (tid == 0) {
+            double a = 0.0, q = 0.0;
+            for (int k = 0; k < n; ++k) {
+                const double mk = srt[k];
+                a = __dadd_rn(a, mk);
+                q = __dadd_rn(q, __dmul_rn(mk, mk));
+                accA[k] = a;
+                accQ[k] = q;
+            }
+        }
+        __syncthreads();
+        const double target = __dmul_rn(delta, accA[n - 1]);
+        // first interval [m_(k), m_(k+1)] whose right end meets the budget
+        for (int k = tid; k < n; k += kSelThreads) {
+            const double hi = (k + 1 < n) ? srt[k + 1] : __builtin_inf();
+            const double f_hi = __dsub_rn(accA[k], __ddiv_rn(accQ[k], hi));
+            if (f_hi >= target) atomicMin(&s_kstar, k);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const int k = s_kstar;
+            s_tau = __ddiv_rn(accQ[k], __dsub_rn(accA[k], target));
+        }
+    } else if (tid == 0) {
+        if (nonfinite) {
+            s_tau = __builtin_nan("");
+        } else if (n == 0) {
+            s_tau = __builtin_inf();
+        } else {  // delta == 0: tau = smallest positive mass
+            double mn = __builtin_inf();
+            for (int i = 0; i < nqb; ++i) {
+                const double mi = m[i];
+                if (mi > 0.0 && mi < mn) mn = mi;
+            }
+            s_tau = mn;
+        }
+    }
+    __syncthreads();
+    const double tau = s_tau;
+
+    // draw, weights and ascending compaction, 1024 blocks per round
+    const int lane = tid & 63, wave = tid >> 6;
+    float* wout = block_w + (size_t)bh * nqb;
+    int32_t* kout = kept_idx + (size_t)bh * nqb;
+    for (int base = 0; base < nqb; base += kSelThreads) {
+        const int i = base + tid;
+        bool keep = false;
+        if (i < nqb) {
+            const double mi = m[i];
+            double p;
+            if (nonfinite) p = 1.0;
+            else if (mi == 0.0) p = 0.0;
+            else p = fmin(1.0, __ddiv_rn(mi, tau));
+            const uint64_t x0 = philox_first_word((uint64_t)i, (uint64_t)h, (uint64_t)b, 0ull, seed, 0ull);
+            const double u = (double)(x0 >> 11) * 0x1p-53;
+            keep = u < p;
+            wout[i] = keep ? (float)__ddiv_rn(1.0, p) : 0.0f;
+        }
+        const uint64_t ballot = __ballot(keep);
+        const int before = __popcll(ballot & ((1ull << lane) - 1ull));
+        if (lane == 0) s_wave[wave] = __popcll(ballot);
+        __syncthreads();
+        int off = s_base;
+        for (int w = 0; w < wave; ++w) off += s_wave[w];
+        if (keep) kout[off + before] = i;
+        __syncthreads();
+        if (tid == 0) {
+            int tot = 0;
+            for (int w = 0; w < kSelThreads / 64; ++w) tot += s_wave[w];
+            s_base += tot;
+        }
+        __syncthreads();
+    }
+    const int count = s_base;
+    for (int i = count + tid; i < nqb; i += kSelThreads) kout[i] = -1;
+    if (tid == 0) {
+        kept_count[bh] = count;
+        tau_out[bh] = tau;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T>
+static hipError_t launch_mass(const Problem& pb, const void* o, const void* dout, float* D,
+                              double* mass, hipStream_t st) {
+    const unsigned nblk = (unsigned)((size_t)pb.B * pb.Hq * pb.nqb);
+    const int L = pb.block * pb.d;
+    const T* po = static_cast<const T*>(o);
+    const T* pd = static_cast<const T*>(dout);
+#define LF_MASS(LL, DD)                                                                     \
+    if (L == LL && pb.d == DD) {                                                            \
+        hipLaunchKernelGGL((mass_d_kernel<T, LL, DD>), dim3(nblk), dim3(256), 0, st, po, pd, \
+                           D, mass);                                                        \
+        return hipGetLastError();                                                           \
+    }
+    LF_MASS(4096, 64)
+    LF_MASS(8192, 64)
+    LF_MASS(8192, 128)
+    LF_MASS(16384, 128)
+#undef LF_MASS
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_select(const Problem& pb, const void* o, const void* dout, double delta,
+                         uint64_t seed, float* D, double* mass, double* tau, float* block_w,
+                         int32_t* kept_idx, int32_t* kept_count, hipStream_t st) {
+    hipError_t e = pb.bf16 ? launch_mass<bf16>(pb, o, dout, D, mass, st)
+                           : launch_mass<float>(pb, o, dout, D, mass, st);
+    if (e != hipSuccess) return e;
+    int P = 1;
+    while (P < pb.nqb) P <<= 1;
+    const size_t lds = 3 * (size_t)P * sizeof(double);
+    if (lds > 65536) {
+        e = hipFuncSetAttribute((const void*)tau_select_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(tau_select_kernel, dim3((unsigned)(pb.B * pb.Hq)), dim3(kSelThreads), lds,
+                       st, mass, delta, seed, pb.Hq, pb.nqb, P, tau, block_w, kept_idx,
+                       kept_count);
+    return hipGetLastError();
+}
+
+}  // namespace lf

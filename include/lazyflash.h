@@ -1,0 +1,160 @@
+/*
+ * lazyflash.h -- C ABI of liblazyflash.so: LazyFlash-style attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method (the LazyFlash journal entry on gyom.fr, "LazyFlash allège la
+ * rétropropagation de l'attention, 5,72 fois"):
+ *   - the forward is ordinary exact FlashAttention and is left dense
+ *     (section "Le passage arrière fait deux fois le travail du passage
+ *     avant");
+ *   - the backward ranks query blocks by the norm of their output gradient,
+ *     keeps each block with a probability set by a budget delta on the
+ *     discarded gradient mass, reweights kept blocks so the gradient stays
+ *     unbiased in expectation, and never loads or computes the skipped tiles
+ *     (section "Un budget sur la masse de gradient, et un tirage qui garde le
+ *     gradient non biaisé");
+ *   - the backward kernel consumes per-block weights directly (section
+ *     "Trois tailles de modèle, 19 découpages sur 21").
+ *
+ * The exact keep rule implemented here (the pages fix the idea, not the rule):
+ *   m[b,h,i] = ||dO[b,h,block i]||_F^2 in float64, summed by the halving tree
+ *              over the row-major flattening of the block;
+ *   p_i      = 0 if m_i == 0, else min(1, m_i / tau);
+ *   tau      = root of sum_i (1 - p_i) m_i = delta * sum_i m_i per (b, h)
+ *              (tau = smallest positive mass when delta == 0, +inf when every
+ *              mass is zero, NaN when a mass is not finite: then every block
+ *              is kept with weight 1);
+ *   u_i      = (x0 >> 11) * 2^-53, x0 = first word of Philox4x64-10 with key
+ *              (seed, 0) and counter (i, h, b, 0);
+ *   keep_i   = u_i < p_i;   w_i = (float)(1.0 / p_i) if kept, else 0.
+ * The sparse gradient equals the dense gradient of dO' = keep * w * dO.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major and contiguous: Q, O, dO, dQ are [B, Hq, N, d],
+ *     K, V, dK, dV are [B, Hkv, N, d] (d fastest); LSE and D are [B, Hq, N].
+ *     Query head h reads key/value head h / (Hq / Hkv).
+ *   - All tensor pointers are DEVICE pointers owned by the caller; outputs are
+ *     fully overwritten (never accumulated into).  The library allocates
+ *     nothing and keeps no state between calls; work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and the call returns without
+ *     waiting for it.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns LF_EINVAL (malformed) or LF_EUNSUPPORTED (valid
+ *     but outside what the kernels implement) and launches nothing.  A failed
+ *     launch returns LF_EHIP.  lf_last_error() describes the last failure of
+ *     the calling thread.
+ *   - An empty problem (batch == 0 or seqlen == 0) is valid and enqueues
+ *     nothing; its tensor pointers may then be NULL.
+ *   - Supported: dtype LF_BF16 or LF_F32, head_dim 64 or 128, block 64 or 128,
+ *     seqlen a multiple of block, seqlen / block <= 4096, heads_q a multiple
+ *     of heads_kv, finite scale.
+ */
+#ifndef LAZYFLASH_H
+#define LAZYFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LF_OK = 0,
+    LF_EINVAL = 1,        /* malformed arguments (null pointer, bad shape, delta) */
+    LF_EUNSUPPORTED = 2,  /* well-formed but not implemented (head_dim, block, ...) */
+    LF_EHIP = 3           /* the HIP runtime reported an error at launch */
+} lf_status;
+
+typedef enum { LF_BF16 = 0, LF_F32 = 1 } lf_dtype;
+
+typedef struct {
+    int32_t batch;      /* B */
+    int32_t heads_q;    /* Hq: query heads */
+    int32_t heads_kv;   /* Hkv: key/value heads, divides Hq */
+    int32_t seqlen;     /* N: queries = keys (self-attention) */
+    int32_t head_dim;   /* d */
+    int32_t block;      /* query-block size of the selection, rows */
+    int32_t causal;     /* nonzero: query i sees keys j <= i */
+    float scale;        /* softmax scale, usually 1/sqrt(d) */
+    int32_t dtype;      /* lf_dtype of Q, K, V, O, dO, dQ, dK, dV */
+} lf_shape;
+
+/*
+ * Dense attention forward (FlashAttention tiling, exact softmax).
+ * The forward is unchanged by the method: see the section "Le passage arrière
+ * fait deux fois le travail du passage avant" of the LazyFlash entry, and the
+ * FlashAttention course page on voce.life, section "Le mécanisme".
+ *   q [B,Hq,N,d], k, v [B,Hkv,N,d]  (dtype)            in
+ *   o [B,Hq,N,d] (dtype)                               out: softmax(scale q k^T) v
+ *   lse [B,Hq,N] float32                               out: natural-log logsumexp
+ *                                                           of each scaled score row
+ */
+lf_status lf_attn_fwd(const lf_shape* shape, const void* q, const void* k, const void* v,
+                      void* o, float* lse, void* stream);
+
+/*
+ * Block selection: masses, budget tau, Philox draw, weights, compaction.
+ * Section "Un budget sur la masse de gradient, et un tirage qui garde le
+ * gradient non biaisé" of the LazyFlash entry; the rule is stated above.
+ *   o, dout [B,Hq,N,d] (dtype)                         in
+ *   delta in [0, 1), seed                              in
+ *   D [B,Hq,N] float32                                 out: rowsum(dout * o)
+ *   mass [B,Hq,nqb] float64                            out: block masses (bit-exact)
+ *   tau [B,Hq] float64                                 out: per-head threshold
+ *   block_w [B,Hq,nqb] float32                         out: 1/p if kept, else 0
+ *   kept_idx [B,Hq,nqb] int32                          out: kept blocks ascending,
+ *                                                           then -1 padding
+ *   kept_count [B,Hq] int32                            out: number of kept blocks
+ * nqb = seqlen / block.  Returns LF_EINVAL for delta outside [0, 1) or NaN.
+ */
+lf_status lf_block_select(const lf_shape* shape, const void* o, const void* dout,
+                          double delta, uint64_t seed, float* D, double* mass, double* tau,
+                          float* block_w, int32_t* kept_idx, int32_t* kept_count,
+                          void* stream);
+
+/*
+ * Block-sparse attention backward over the kept query blocks only.
+ * Sections "Un budget sur la masse de gradient..." (skipped tiles are never
+ * loaded nor computed) and "Trois tailles de modèle, 19 découpages sur 21"
+ * (the backward kernel consumes the per-block weights) of the LazyFlash entry.
+ *   q, k, v, dout (dtype), lse, D (float32)            in: as above
+ *   kept_idx, kept_count, block_w                      in: from lf_block_select
+ *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d] (dtype)          out: gradient of dO' =
+ *                                                           keep*w*dO; rows of
+ *                                                           skipped blocks of dq
+ *                                                           are exact zeros
+ *   workspace, workspace_bytes                         scratch device memory of at
+ *                                                      least lf_bwd_workspace_bytes()
+ *                                                      bytes, contents undefined on
+ *                                                      entry and on return
+ * Passing every block kept with weight 1 (lf_block_select with delta = 0)
+ * gives the dense backward through the same kernels.
+ */
+lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const void* v,
+                      const float* lse, const void* dout, const float* D,
+                      const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Bytes of device workspace lf_attn_bwd needs for `shape` (0 if the shape is
+ * invalid).  Currently the float32 dq accumulator: B*Hq*N*d*4 bytes. */
+size_t lf_bwd_workspace_bytes(const lf_shape* shape);
+
+/* Static, human-readable name of a status code. */
+const char* lf_status_str(lf_status status);
+
+/* Description of the last failure on the calling thread ("" if none).  The
+ * string is owned by the library and valid until the thread's next call. */
+const char* lf_last_error(void);
+
+/* ABI version of this header, for run-time checks by bindings. */
+int32_t lf_abi_version(void);
+
+#define LF_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAZYFLASH_H */

@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: it loads, exports every declared entry
+point, and rejects malformed arguments before touching any GPU state (so these
+run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_backward_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lazyflash.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lf_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bd.load()
+    names = declared_functions()
+    assert set(names) == set(bd.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lf_[a-z_0-9]+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_abi_version_and_status_names():
+    lib = bd.load()
+    assert lib.lf_abi_version() == bd.ABI_VERSION
+    assert lib.lf_status_str(0) == b"LF_OK"
+    assert lib.lf_status_str(1) == b"LF_EINVAL"
+    assert lib.lf_status_str(2) == b"LF_EUNSUPPORTED"
+    assert lib.lf_status_str(3) == b"LF_EHIP"
+    assert lib.lf_status_str(99) == b"unknown lf_status"
+
+
+def _shape(**kw):
+    base = dict(batch=1, heads_q=4, heads_kv=2, seqlen=256, head_dim=128, block=128, causal=1,
+                scale=128 ** -0.5, dtype=bd.LF_BF16)
+    base.update(kw)
+    return bd.LfShape(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+def _fwd(lib, shp, ptr=FAKE):
+    return lib.lf_attn_fwd(ctypes.byref(shp) if shp is not None else None, ptr, ptr, ptr, ptr,
+                           ptr, NULL)
+
+
+def _sel(lib, shp, delta, ptr=FAKE):
+    return lib.lf_block_select(ctypes.byref(shp), ptr, ptr, delta, 0, ptr, ptr, ptr, ptr, ptr,
+                               ptr, NULL)
+
+
+def _bwd(lib, shp, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE):
+    return lib.lf_attn_bwd(ctypes.byref(shp), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                           ptr, ptr, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=3, heads_kv=2), bd.LF_EINVAL),
+    (dict(heads_kv=0), bd.LF_EINVAL),
+    (dict(batch=-1), bd.LF_EINVAL),
+    (dict(dtype=7), bd.LF_EINVAL),
+    (dict(scale=math.inf), bd.LF_EINVAL),
+    (dict(scale=math.nan), bd.LF_EINVAL),
+    (dict(head_dim=96), bd.LF_EUNSUPPORTED),
+    (dict(block=32), bd.LF_EUNSUPPORTED),
+    (dict(seqlen=200), bd.LF_EUNSUPPORTED),
+    (dict(seqlen=128 * 4097), bd.LF_EUNSUPPORTED),
+])
+def test_bad_shapes_rejected_by_every_entry_point(kw, status):
+    lib = bd.load()
+    shp = _shape(**kw)
+    assert _fwd(lib, shp) == status
+    assert lib.lf_last_error() != b""
+    assert _sel(lib, shp, 0.1) == status
+    assert _bwd(lib, shp) == status
+    assert lib.lf_bwd_workspace_bytes(ctypes.byref(shp)) == 0
+
+
+def test_null_shape_and_null_pointers():
+    lib = bd.load()
+    assert lib.lf_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == bd.LF_EINVAL
+    assert _fwd(lib, _shape(), ptr=NULL) == bd.LF_EINVAL
+    assert b"NULL" in lib.lf_last_error()
+    assert _sel(lib, _shape(), 0.1, ptr=NULL) == bd.LF_EINVAL
+    assert _bwd(lib, _shape(), ptr=NULL) == bd.LF_EINVAL
+
+
+@pytest.mark.parametrize("delta", [-0.01, 1.0, 2.0, math.nan, math.inf])
+def test_select_rejects_bad_delta(delta):
+    lib = bd.load()
+    assert _sel(lib, _shape(), delta) == bd.LF_EINVAL
+    assert b"delta" in lib.lf_last_error()
+
+
+def test_workspace_size_and_check():
+    lib = bd.load()
+    shp = _shape()
+    need = lib.lf_bwd_workspace_bytes(ctypes.byref(shp))
+    assert need == 1 * 4 * 256 * 128 * 4
+    assert _bwd(lib, shp, ws=NULL) == bd.LF_EINVAL
+    assert _bwd(lib, shp, ws_bytes=need - 1) == bd.LF_EINVAL
+    assert b"workspace" in lib.lf_last_error()
+    # the float32 path needs none
+    assert lib.lf_bwd_workspace_bytes(ctypes.byref(_shape(dtype=bd.LF_F32))) == 0
+
+
+def test_empty_problems_are_noops():
+    lib = bd.load()
+    for kw in (dict(batch=0), dict(seqlen=0)):
+        shp = _shape(**kw)
+        assert _fwd(lib, shp, ptr=NULL) == bd.LF_OK
+        assert _sel(lib, shp, 0.1, ptr=NULL) == bd.LF_OK
+        assert _bwd(lib, shp, ws=NULL, ws_bytes=0, ptr=NULL) == bd.LF_OK
+        assert lib.lf_bwd_workspace_bytes(ctypes.byref(shp)) == 0
+    # delta is still checked on an empty problem
+    assert _sel(lib, _shape(batch=0), 1.5, ptr=NULL) == bd.LF_EINVAL
+
+
+def test_binding_rejects_unsupported_dtype():
+    import torch
+    with pytest.raises(bd.LazyFlashError):
+        bd.make_shape(1, 1, 1, 64, 64, 64, True, 0.1, torch.float16)

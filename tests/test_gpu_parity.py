@@ -1,0 +1,140 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Kept sets (mass, tau, block weights, kept_idx, kept_count) must be bit-identical;
+O, dQ, dK, dV within max-abs-rel 2e-2 (bf16) / 1e-4 (fp32), LSE within 1e-3 /
+1e-5 absolute, D within the output tolerance.  Small shapes compare every
+element; the full workload shapes compare the whole kept set plus sampled
+outputs the oracle computes exactly (one GQA group)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_backward_amd.synth import CONFIGS, Config, make_inputs, to_f64
+from tests.parity_helpers import (LSE_TOL, TOL, check_d_rows, check_fwd_rows,
+                                  check_select_exact, host, max_abs_rel, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_f32": (CONFIGS["tiny"], 0.1),
+    "bf16_gqa_d128_b128": (Config("s1", 1, 4, 2, 512, 128, "bf16", True, 128, 1.5), 0.1),
+    "bf16_dense_delta0": (Config("s2", 1, 4, 2, 512, 128, "bf16", True, 128, 1.5), 0.0),
+    "bf16_ragged_d64_b64": (Config("s3", 2, 4, 1, 448, 64, "bf16", True, 64, 1.0), 0.2),
+    "bf16_noncausal_d64": (Config("s4", 2, 2, 2, 384, 64, "bf16", False, 64, 0.5), 0.1),
+    "bf16_d128_b64_ragged": (Config("s5", 1, 2, 1, 320, 128, "bf16", True, 64, 1.5), 0.1),
+    "bf16_gqa8_d64_b128": (Config("s6", 1, 8, 1, 512, 64, "bf16", True, 128, 1.5), 0.05),
+    "bf16_noncausal_d128_b128": (Config("s7", 1, 4, 4, 256, 128, "bf16", False, 128, 1.0), 0.3),
+    "f32_noncausal_d128": (Config("s8", 1, 2, 1, 128, 128, "f32", False, 64, 1.0), 0.2),
+    "bf16_boosted_heavy": (Config("s9", 1, 4, 2, 1024, 128, "bf16", True, 128, 2.0,
+                                  boost_frac=0.1, boost=20.0), 0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(name):
+    cfg, delta = SMALL[name]
+    print(f"[parity] {name} {cfg} delta={delta}", flush=True)
+    inp = make_inputs(cfg, 0)
+    gpu = run_gpu(cfg, inp, delta, seed=0)
+    ref_sel = check_select_exact(cfg, inp, gpu, delta, 0)
+    q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    o_ref, lse_ref = oracle.attn_fwd(q64, k64, v64, cfg.scale, cfg.causal)
+    tol = TOL[cfg.dtype]
+    assert max_abs_rel(host(gpu["o"]), o_ref) <= tol
+    assert np.abs(host(gpu["lse"]) - lse_ref).max() <= LSE_TOL[cfg.dtype]
+    d_ref = (d64 * o_ref).sum(axis=-1)
+    assert max_abs_rel(host(gpu["sel"]["D"]), d_ref) <= tol
+    dq, dk, dv = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, ref_sel["keep"],
+                                        ref_sel["w"], cfg.scale, cfg.causal)
+    errs = [max_abs_rel(host(gpu[n]), r) for n, r in (("dq", dq), ("dk", dk), ("dv", dv))]
+    print(f"[parity] {name} kept={ref_sel['keep'].mean():.3f} errs={errs}", flush=True)
+    assert max(errs) <= tol, errs
+    # rows of skipped blocks of dq are exact zeros
+    skipped = np.repeat(~ref_sel["keep"], cfg.block, axis=2)
+    assert np.all(host(gpu["dq"])[skipped] == 0.0)
+
+
+_CACHE = {}
+
+
+def _full_inputs(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        cfg = CONFIGS[name]
+        inp = make_inputs(cfg, 0)
+        _CACHE[name] = (cfg, inp)
+    return _CACHE[name]
+
+
+FULL = [(n, dl) for n in ("mid", "headline", "long", "noncausal") for dl in CONFIGS[n].deltas]
+
+
+@pytest.mark.parametrize("name,delta", FULL)
+def test_full_size_parity(name, delta):
+    cfg, inp = _full_inputs(name)
+    print(f"[parity-full] {name} delta={delta}", flush=True)
+    gpu = run_gpu(cfg, inp, delta, seed=0)
+    ref_sel = check_select_exact(cfg, inp, gpu, delta, 0)
+    kept_frac = float(ref_sel["keep"].mean())
+    G = cfg.Hq // cfg.Hkv
+    b, g = cfg.B - 1, cfg.Hkv // 2
+    heads = [(b, g * G + x) for x in range(G)]
+    rng = np.random.Generator(np.random.PCG64(1))
+    rows = np.unique(np.concatenate([[0, 1, cfg.N - 1], rng.integers(0, cfg.N, 60)]))
+    err_o, err_l = check_fwd_rows(cfg, inp, gpu, heads[:2], rows)
+    assert err_o <= TOL[cfg.dtype] and err_l <= LSE_TOL[cfg.dtype], (err_o, err_l)
+    assert check_d_rows(cfg, inp, gpu, heads[:2], rows) <= TOL[cfg.dtype]
+
+    q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    keep = ref_sel["keep"]
+    nqb = cfg.nqb
+    if cfg.causal:
+        # dQ of sampled kept blocks (each block's dq depends on that block
+        # only), and dK/dV of the keys at and after block jt: under the causal
+        # mask only query blocks >= jt reach them, and all of those that are
+        # kept are in the sample.  jt is chosen so that about six kept blocks
+        # of the group lie at or after it.
+        kept_all = sorted({int(i) for bb, h in heads for i in np.nonzero(keep[bb, h])[0]})
+        jt = kept_all[-min(6, len(kept_all))] if kept_all else nqb - 1
+        sample = np.zeros_like(keep)
+        for bb, h in heads:
+            kept = np.nonzero(keep[bb, h])[0]
+            pick = set(rng.choice(kept, min(3, kept.size), replace=False).tolist())
+            pick |= {int(i) for i in kept if i >= jt}
+            for i in pick:
+                sample[bb, h, i] = True
+        dq, dk, dv = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, sample, ref_sel["w"],
+                                            cfg.scale, cfg.causal, heads=heads)
+        sel_rows = []
+        for bb, h in heads:
+            for i in np.nonzero(sample[bb, h])[0]:
+                sel_rows.append((bb, h, i))
+        got = np.stack([host(gpu["dq"][bb, h, i * cfg.block:(i + 1) * cfg.block])
+                        for bb, h, i in sel_rows])
+        want = np.stack([dq[bb, h, i * cfg.block:(i + 1) * cfg.block] for bb, h, i in sel_rows])
+        e_dq = max_abs_rel(got, want)
+        tail = slice(jt * cfg.block, cfg.N)
+        assert np.abs(dk[b, g, tail]).max() > 0
+        e_dk = max_abs_rel(host(gpu["dk"][b, g, tail]), dk[b, g, tail])
+        e_dv = max_abs_rel(host(gpu["dv"][b, g, tail]), dv[b, g, tail])
+    else:
+        dq, dk, dv = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, keep, ref_sel["w"],
+                                            cfg.scale, cfg.causal, heads=heads)
+        hs = [h for _, h in heads]
+        e_dq = max_abs_rel(host(gpu["dq"][b, hs]), dq[b, hs])
+        e_dk = max_abs_rel(host(gpu["dk"][b, g]), dk[b, g])
+        e_dv = max_abs_rel(host(gpu["dv"][b, g]), dv[b, g])
+    print(f"[parity-full] {name} delta={delta} kept={kept_frac:.4f} fwd={err_o:.2e} "
+          f"dq={e_dq:.2e} dk={e_dk:.2e} dv={e_dv:.2e}", flush=True)
+    assert max(e_dq, e_dk, e_dv) <= TOL[cfg.dtype]
+    # any size: each row of dS sums to zero, so the keys' dK sum to zero; the
+    # keys' dV sum to the weighted kept dO rows (per kv head, all query heads)
+    dk_all = host(gpu["dk"]).sum(axis=2)
+    dv_all = host(gpu["dv"]).sum(axis=2)
+    wrow = np.repeat(ref_sel["keep"] * ref_sel["w"].astype(np.float64), cfg.block, axis=2)
+    want_dv = (d64 * wrow[..., None]).sum(axis=2).reshape(cfg.B, cfg.Hkv, G, cfg.d).sum(axis=2)
+    scale_dk = np.abs(host(gpu["dk"])).max() * np.sqrt(cfg.N)
+    assert np.abs(dk_all).max() <= 2e-2 * scale_dk
+    assert max_abs_rel(dv_all, want_dv) <= 2e-2
+    torch.cuda.empty_cache()
