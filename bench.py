@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of LazyFlash-style attention on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch: dense forward
+(O, LSE), block selection (masses, D, tau, draw, compaction), sparse backward
+(prepare, tile walk, finalize), each with a fresh selection seed.  Inputs are
+resident in HBM before timing starts.  The headline metric is the attention
+backward of one layer -- select + backward, the part the method changes -- as
+effective dense-equivalent TFLOP/s (dense backward FLOPs / measured time);
+ms per microbatch and the delta sweep ride along.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+
+    python bench.py [--steps K] [--warmup W] [--config headline] [--delta 0.1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+BWD_SOURCE = os.path.join(ROOT, "block_sparse_backward_amd", "csrc", "lf_bwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="headline")
+    ap.add_argument("--delta", type=float, default=None, help="main delta (default 0.1)")
+    ap.add_argument("--sweep-steps", type=int, default=5,
+                    help="steps per extra delta of the sweep (0: no sweep)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+                    help="approximate CPU seconds spent on the oracle baseline sample")
+    return ap.parse_args()
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the method needs no exchange "
+              "between GPUs inside the attention backward); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_backward_amd import binding as bd
+    from block_sparse_backward_amd import metrics
+    from block_sparse_backward_amd.synth import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    bd.load()  # fail loudly if the HIP library is missing
+    cfg = CONFIGS[args.config]
+    main_delta = args.delta if args.delta is not None else (0.1 if 0.1 in cfg.deltas else cfg.deltas[-1])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] generating {cfg}")
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg, 0)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f}s)")
+
+    # preallocated outputs: no allocation inside the timed region
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    shp = bd.make_shape(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d, cfg.block, cfg.causal, cfg.scale,
+                        cfg.torch_dtype)
+    ws = torch.empty(max(bd.bwd_workspace_bytes(shp), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_steps(delta, seeds):
+        """Runs one step per seed; returns per-step event pairs and selections."""
+        sels = [bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev) for _ in seeds]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in seeds]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for seed, sel, ev in zip(seeds, sels, evs):
+            ev[0].record(stream)
+            bd.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, block=cfg.block, out=(o, lse))
+            ev[1].record(stream)
+            bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
+                            scale=cfg.scale, heads_kv=cfg.Hkv, out=sel)
+            ev[2].record(stream)
+            common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, workspace=ws,
+                          out=(dq, dk, dv))
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_PREPARE, **common)
+            ev[3].record(stream)
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_MAIN, **common)
+            ev[4].record(stream)
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_FINALIZE, **common)
+            ev[5].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(5)] for e in evs])
+        flops = [metrics.bwd_flops_kept(s["block_w"].cpu().numpy(), cfg.N, cfg.d, cfg.block,
+                                        cfg.causal) for s in sels]
+        kept = [float((s["block_w"] != 0).float().mean().item()) for s in sels]
+        return wall, ms, np.array(flops, dtype=np.float64), np.array(kept)
+
+    F_dense = metrics.bwd_flops_dense(cfg.B, cfg.Hq, cfg.N, cfg.d, cfg.causal)
+    F_fwd = metrics.fwd_flops(cfg.B, cfg.Hq, cfg.N, cfg.d, cfg.causal)
+
+    log(f"[bench] warmup {args.warmup} steps, delta={main_delta}")
+    run_steps(main_delta, list(range(10_000, 10_000 + args.warmup)))
+    log(f"[bench] timing {args.steps} steps, delta={main_delta}")
+    wall, ms, flops, kept = run_steps(main_delta, list(range(args.steps)))
+    # columns: fwd, select, bwd prepare, bwd main, bwd finalize
+    t_fwd, t_sel, t_prep, t_main, t_fin = ms.mean(axis=0)
+    t_bwd = t_prep + t_main + t_fin
+    t_attn_bwd = t_sel + t_bwd
+    per_step_attn = ms[:, 1:].sum(axis=1)
+    value = F_dense / (t_attn_bwd * 1e-3) / 1e12
+    log(f"[bench] fwd {t_fwd:.3f} ms, select {t_sel:.3f} ms, bwd {t_bwd:.3f} ms "
+        f"(main {t_main:.3f}), kept {kept.mean():.4f}")
+
+    sweep = {}
+    for dl in cfg.deltas:
+        if dl == main_delta:
+            sweep[dl] = (ms, flops, kept)
+            continue
+        if args.sweep_steps <= 0:
+            continue
+        log(f"[bench] sweep delta={dl}")
+        run_steps(dl, [20_000])
+        _, ms_d, fl_d, kept_d = run_steps(dl, list(range(args.sweep_steps)))
+        sweep[dl] = (ms_d, fl_d, kept_d)
+    sweep_out = []
+    for dl in sorted(sweep):
+        ms_d, fl_d, kept_d = sweep[dl]
+        attn_ms = float(ms_d[:, 1:].sum(axis=1).mean())
+        sweep_out.append(dict(
+            delta=dl, steps=int(ms_d.shape[0]), select_ms=round(float(ms_d[:, 1].mean()), 4),
+            bwd_ms=round(float(ms_d[:, 2:].sum(axis=1).mean()), 4),
+            attn_bwd_ms=round(attn_ms, 4),
+            attn_bwd_ms_min=round(float(ms_d[:, 1:].sum(axis=1).min()), 4),
+            attn_bwd_ms_max=round(float(ms_d[:, 1:].sum(axis=1).max()), 4),
+            eff_tflops=round(F_dense / (attn_ms * 1e-3) / 1e12, 2),
+            kept_fraction=round(float(kept_d.mean()), 5),
+            kept_work_fraction=round(float(fl_d.mean() / F_dense), 5),
+            main_kernel_tflops_on_kept=round(float(fl_d.sum() / (ms_d[:, 3].sum() * 1e-3) / 1e12), 2),
+        ))
+    dense_ms = next((s["attn_bwd_ms"] for s in sweep_out if s["delta"] == 0.0), None)
+    speedup = round(dense_ms / t_attn_bwd, 3) if dense_ms else None
+
+    # roofline of the dominant kernel of the measured region: the backward walk
+    achieved = float(flops.sum() / (ms[:, 3].sum() * 1e-3) / 1e12)
+    peak = metrics.MI355X_PEAK["bf16_flops"] / 1e12
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        prof = json.load(open(PROFILE_TRAFFIC))
+        if prof.get("source_sha256") == source_sha(BWD_SOURCE) and \
+                prof.get("workload") == cfg.name and prof.get("delta") == main_delta:
+            traffic = prof.get("bytes_per_launch")
+    roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(achieved / peak, 4), traffic=traffic,
+                    kernel="bwd_bf16_kernel (backward tile walk over kept blocks)",
+                    algorithmic_flops_per_launch=float(flops.mean()))
+    others = dict(
+        fwd=dict(bound="mfma", achieved=round(F_fwd / (t_fwd * 1e-3) / 1e12, 2), peak=peak,
+                 unit="TFLOP/s"),
+        select_mass_pass=dict(bound="hbm", bytes_per_launch=2 * q.numel() * q.element_size(),
+                              unit="GB/s", peak=8000.0,
+                              note="select = streaming pass (dO, O read) + per-head tau kernel; "
+                                   "time includes both"),
+    )
+    others["select_mass_pass"]["achieved_incl_tau"] = round(
+        others["select_mass_pass"]["bytes_per_launch"] / (t_sel * 1e-3) / 1e9, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, main_delta, args.cpu_budget_s, metrics)
+
+    out = {
+        "metric": f"attention-bwd effective dense-equivalent TFLOP/s (select + sparse bwd, one "
+                  f"layer) at N={cfg.N}, delta={main_delta}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V, dO with per-row lognormal(0,%g) scale%s; no "
+                "model or dataset" % (cfg.sigma, ", %d%% of blocks x%g" % (
+                    round(100 * cfg.boost_frac), cfg.boost) if cfg.boost_frac else ""),
+        "config": {"workload": f"{cfg.name}: one attention layer, B={cfg.B} Hq={cfg.Hq} "
+                               f"Hkv={cfg.Hkv} N={cfg.N} d={cfg.d} block={cfg.block} "
+                               f"{'causal' if cfg.causal else 'non-causal'}",
+                   "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "N": cfg.N, "d": cfg.d,
+                   "block": cfg.block, "causal": cfg.causal, "delta": main_delta},
+        "attn_bwd_ms_per_microbatch": round(t_attn_bwd, 4),
+        "attn_bwd_ms_min": round(float(per_step_attn.min()), 4),
+        "attn_bwd_ms_max": round(float(per_step_attn.max()), 4),
+        "select_ms": round(t_sel, 4),
+        "bwd_ms": round(t_bwd, 4),
+        "bwd_phases_ms": {"prepare": round(t_prep, 4), "main": round(t_main, 4),
+                          "finalize": round(t_fin, 4)},
+        "fwd_ms": round(t_fwd, 4),
+        "kept_fraction": round(float(kept.mean()), 5),
+        "kept_work_fraction": round(float(flops.mean() / F_dense), 5),
+        "speedup_vs_own_dense": speedup,
+        "fwd_plus_bwd_speedup_vs_own_dense": (
+            round((t_fwd + dense_ms) / (t_fwd + t_attn_bwd), 3) if dense_ms else None),
+        "delta_sweep": sweep_out,
+        "roofline": roofline,
+        "other_kernels": others,
+        "cpu_baseline": cpu,
+        "timing": "HIP events on the launch stream, steady state (caches not flushed); "
+                  "ms_per_step is host wall time of whole steps (fwd+select+bwd)",
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, inp, delta, budget_s, metrics):
+    """The oracle, timed on the host cores on whole GQA groups of the same
+    workload until about `budget_s` seconds are spent."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    import oracle
+    from block_sparse_backward_amd.synth import to_f64
+
+    G = cfg.Hq // cfg.Hkv
+    spent = 0.0
+    heads_done = 0
+    groups = [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
+    log(f"[bench] cpu baseline: oracle on whole GQA groups, ~{budget_s}s budget")
+    for b, g in groups:
+        hs = slice(g * G, (g + 1) * G)
+        q64 = to_f64(inp["q"][b:b + 1, hs])
+        d64 = to_f64(inp["dout"][b:b + 1, hs])
+        k64 = to_f64(inp["k"][b:b + 1, g:g + 1])
+        v64 = to_f64(inp["v"][b:b + 1, g:g + 1])
+        t0 = time.perf_counter()
+        mass = oracle.block_masses(d64, cfg.block)
+        sel = oracle.select(mass, delta, 0)
+        oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, sel["keep"], sel["w"], cfg.scale,
+                               cfg.causal)
+        spent += time.perf_counter() - t0
+        heads_done += G
+        if spent >= budget_s:
+            break
+    f_sample = metrics.bwd_flops_dense(1, heads_done, cfg.N, cfg.d, cfg.causal)
+    return {"value": round(f_sample / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads_done} of {cfg.B * cfg.Hq} query heads ({heads_done // G} GQA "
+                      f"groups), select + sparse backward at delta={delta}, seed 0, fp64 NumPy; "
+                      f"{spent:.1f} s; value = dense-equivalent FLOPs of the sampled heads / time",
+            "seconds": round(spent, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -12,14 +12,15 @@ import os
 import torch
 
 __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block_select",
-           "attn_bwd", "bwd_workspace_bytes", "EXPORTED_SYMBOLS", "LIB_PATH"]
+           "select_outputs", "attn_bwd", "bwd_workspace_bytes", "EXPORTED_SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
 ABI_VERSION = 1
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
-EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_bwd_workspace_bytes",
-                    "lf_status_str", "lf_last_error", "lf_abi_version")
+EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_attn_bwd_phases",
+                    "lf_bwd_workspace_bytes", "lf_status_str", "lf_last_error", "lf_abi_version")
+BWD_PREPARE, BWD_MAIN, BWD_FINALIZE, BWD_ALL = 1, 2, 4, 7
 
 
 class LazyFlashError(RuntimeError):
@@ -56,6 +57,9 @@ def load(path=LIB_PATH):
     lib.lf_block_select.restype = I32
     lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.lf_attn_bwd.restype = I32
+    lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z,
+                                       ctypes.c_uint32, P]
+    lib.lf_attn_bwd_phases.restype = I32
     lib.lf_bwd_workspace_bytes.argtypes = [S]
     lib.lf_bwd_workspace_bytes.restype = Z
     lib.lf_status_str.argtypes = [I32]
@@ -113,25 +117,44 @@ def _shape_from(q, k, block, causal, scale):
     return make_shape(B, Hq, Hkv, N, d, block, causal, scale, q.dtype), scale
 
 
-def attn_fwd(q, k, v, causal=True, scale=None, block=128):
-    """Dense forward: returns (o [B,Hq,N,d] like q, lse [B,Hq,N] float32)."""
+def attn_fwd(q, k, v, causal=True, scale=None, block=128, out=None):
+    """Dense forward: returns (o [B,Hq,N,d] like q, lse [B,Hq,N] float32).
+    `out` optionally gives preallocated (o, lse)."""
     lib = load()
     shp, _ = _shape_from(q, k, block, causal, scale)
     dev = q.device
     _need(q, "q", q.shape, q.dtype, dev)
     _need(k, "k", (shp.batch, shp.heads_kv, shp.seqlen, shp.head_dim), q.dtype, dev)
     _need(v, "v", k.shape, q.dtype, dev)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev))
+    o, lse = out
+    _need(o, "o", q.shape, q.dtype, dev)
+    _need(lse, "lse", q.shape[:3], torch.float32, dev)
     _check(lib, lib.lf_attn_fwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                 _stream(dev)))
     return o, lse
 
 
-def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads_kv=None):
+def select_outputs(B, Hq, N, block, device):
+    """Preallocated output tensors of block_select."""
+    nqb = N // block if block else 0
+    return dict(
+        D=torch.empty((B, Hq, N), dtype=torch.float32, device=device),
+        mass=torch.empty((B, Hq, nqb), dtype=torch.float64, device=device),
+        tau=torch.empty((B, Hq), dtype=torch.float64, device=device),
+        block_w=torch.empty((B, Hq, nqb), dtype=torch.float32, device=device),
+        kept_idx=torch.empty((B, Hq, nqb), dtype=torch.int32, device=device),
+        kept_count=torch.empty((B, Hq), dtype=torch.int32, device=device),
+    )
+
+
+def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads_kv=None,
+                 out=None):
     """Masses, tau, draw and compaction.  Returns a dict of device tensors:
     D [B,Hq,N] f32, mass [B,Hq,nqb] f64, tau [B,Hq] f64, block_w [B,Hq,nqb] f32,
-    kept_idx [B,Hq,nqb] i32, kept_count [B,Hq] i32."""
+    kept_idx [B,Hq,nqb] i32, kept_count [B,Hq] i32 (`out`: preallocated dict
+    from select_outputs)."""
     lib = load()
     B, Hq, N, d = o.shape
     shp = make_shape(B, Hq, heads_kv or Hq, N, d, block, causal,
@@ -140,14 +163,14 @@ def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads
     _need(o, "o", o.shape, o.dtype, dev)
     _need(dout, "dout", o.shape, o.dtype, dev)
     nqb = N // block if block else 0
-    out = dict(
-        D=torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
-        mass=torch.empty((B, Hq, nqb), dtype=torch.float64, device=dev),
-        tau=torch.empty((B, Hq), dtype=torch.float64, device=dev),
-        block_w=torch.empty((B, Hq, nqb), dtype=torch.float32, device=dev),
-        kept_idx=torch.empty((B, Hq, nqb), dtype=torch.int32, device=dev),
-        kept_count=torch.empty((B, Hq), dtype=torch.int32, device=dev),
-    )
+    if out is None:
+        out = select_outputs(B, Hq, N, block, dev)
+    _need(out["D"], "D", (B, Hq, N), torch.float32, dev)
+    _need(out["mass"], "mass", (B, Hq, nqb), torch.float64, dev)
+    _need(out["tau"], "tau", (B, Hq), torch.float64, dev)
+    _need(out["block_w"], "block_w", (B, Hq, nqb), torch.float32, dev)
+    _need(out["kept_idx"], "kept_idx", (B, Hq, nqb), torch.int32, dev)
+    _need(out["kept_count"], "kept_count", (B, Hq), torch.int32, dev)
     _check(lib, lib.lf_block_select(ctypes.byref(shp), _ptr(o), _ptr(dout), float(delta),
                                     ctypes.c_uint64(int(seed) & (2**64 - 1)), _ptr(out["D"]),
                                     _ptr(out["mass"]), _ptr(out["tau"]), _ptr(out["block_w"]),
@@ -160,10 +183,11 @@ def bwd_workspace_bytes(shape):
 
 
 def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, workspace=None,
-             out=None):
+             out=None, phases=BWD_ALL):
     """Sparse backward over the kept blocks of `sel` (the dict of block_select).
     Returns (dq, dk, dv).  `workspace` (uint8 device tensor) and `out`
-    (preallocated (dq, dk, dv)) are optional."""
+    (preallocated (dq, dk, dv)) are optional; `phases` selects a subset of the
+    backward's phases (see lf_attn_bwd_phases)."""
     lib = load()
     shp, _ = _shape_from(q, k, block, causal, scale)
     dev = q.device
@@ -183,9 +207,14 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, worksp
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = out
-    _check(lib, lib.lf_attn_bwd(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(lse),
-                                _ptr(dout), _ptr(sel["D"]), _ptr(sel["kept_idx"]),
-                                _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq), _ptr(dk),
-                                _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                                _stream(dev)))
+    _need(dq, "dq", q.shape, q.dtype, dev)
+    _need(dk, "dk", k.shape, q.dtype, dev)
+    _need(dv, "dv", k.shape, q.dtype, dev)
+    args = (ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(sel["D"]),
+            _ptr(sel["kept_idx"]), _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()))
+    if phases == BWD_ALL:
+        _check(lib, lib.lf_attn_bwd(*args, _stream(dev)))
+    else:
+        _check(lib, lib.lf_attn_bwd_phases(*args, ctypes.c_uint32(phases), _stream(dev)))
     return dq, dk, dv

@@ -116,15 +116,17 @@ lf_status lf_block_select(const lf_shape* s, const void* o, const void* dout, do
                                         kept_count, (hipStream_t)stream));
 }
 
-lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const void* v,
-                      const float* lse, const void* dout, const float* D,
-                      const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+lf_status lf_attn_bwd_phases(const lf_shape* s, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dout, const float* D,
+                             const int32_t* kept_idx, const int32_t* kept_count,
+                             const float* block_w, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, uint32_t phases,
+                             void* stream) {
     lf::Problem pb;
     bool empty;
     lf_status st = check_shape(s, pb, empty);
     if (st != LF_OK) return st;
+    if (phases == 0 || (phases & ~LF_BWD_ALL) != 0) return fail(LF_EINVAL, "bad phase mask");
     if (empty) return hip_status(hipSuccess);
     if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv}))
         return fail(LF_EINVAL, "NULL tensor pointer");
@@ -132,7 +134,17 @@ lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const voi
     if (need && (!workspace || workspace_bytes < need))
         return fail(LF_EINVAL, "workspace missing or smaller than lf_bwd_workspace_bytes()");
     return hip_status(lf::launch_bwd(pb, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq,
-                                     dk, dv, static_cast<float*>(workspace), (hipStream_t)stream));
+                                     dk, dv, static_cast<float*>(workspace), phases,
+                                     (hipStream_t)stream));
+}
+
+lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const void* v,
+                      const float* lse, const void* dout, const float* D,
+                      const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    return lf_attn_bwd_phases(s, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv,
+                              workspace, workspace_bytes, LF_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -409,8 +409,11 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, float* dq_acc, hipStream_t st) {
+                      void* dq, void* dk, void* dv, float* dq_acc, unsigned phases,
+                      hipStream_t st) {
+    const bool prep = phases & 1u, main = phases & 2u, fin = phases & 4u;
     if (!pb.bf16) {
+        if (!main) return hipSuccess;
         dim3 gkv((unsigned)((pb.N + 63) / 64), (unsigned)(pb.B * pb.Hkv));
         dim3 gq((unsigned)((pb.N + 63) / 64), (unsigned)(pb.B * pb.Hq));
 #define LF_F32BWD(DD)                                                                          \
@@ -436,14 +439,18 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     const float sl2 = pb.scale * kLog2e;
 #define LF_BWD(DD, BB, CC)                                                                      \
     if (pb.d == DD && pb.block == BB && (pb.causal != 0) == CC) {                               \
-        hipLaunchKernelGGL((dq_zero_kernel<DD, BB>), dim3(nblocks), dim3(256), 0, st, block_w,  \
-                           dq_acc);                                                             \
-        hipLaunchKernelGGL((bwd_bf16_kernel<DD, BB, CC>), dim3(nwg), dim3(256), 0, st,          \
-                           (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,                 \
-                           (const bf16*)dout, D, kept_idx, kept_count, block_w, (bf16*)dk,      \
-                           (bf16*)dv, dq_acc, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale, sl2); \
-        hipLaunchKernelGGL((dq_convert_kernel<DD, BB>), dim3(nblocks), dim3(256), 0, st,        \
-                           block_w, dq_acc, (bf16*)dq, pb.scale);                               \
+        if (prep)                                                                               \
+            hipLaunchKernelGGL((dq_zero_kernel<DD, BB>), dim3(nblocks), dim3(256), 0, st,       \
+                               block_w, dq_acc);                                                \
+        if (main)                                                                               \
+            hipLaunchKernelGGL((bwd_bf16_kernel<DD, BB, CC>), dim3(nwg), dim3(256), 0, st,      \
+                               (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
+                               (const bf16*)dout, D, kept_idx, kept_count, block_w, (bf16*)dk,  \
+                               (bf16*)dv, dq_acc, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale,  \
+                               sl2);                                                            \
+        if (fin)                                                                                \
+            hipLaunchKernelGGL((dq_convert_kernel<DD, BB>), dim3(nblocks), dim3(256), 0, st,    \
+                               block_w, dq_acc, (bf16*)dq, pb.scale);                           \
         return hipGetLastError();                                                               \
     }
     LF_BWD(64, 64, true)

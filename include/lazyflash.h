@@ -137,6 +137,30 @@ lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * The three phases of lf_attn_bwd, enqueued separately.  Calling
+ * lf_attn_bwd_phases with every bit set is exactly lf_attn_bwd; calling it
+ * once per phase, in order, on one stream, with the same arguments and the
+ * same workspace, gives the same result.  This lets a caller interleave other
+ * work between the phases, or time the tile walk on its own.
+ *   LF_BWD_PREPARE   clear the float32 dq accumulator rows of kept blocks
+ *   LF_BWD_MAIN      walk the kept blocks: dk, dv and the dq accumulator
+ *   LF_BWD_FINALIZE  dq = scale * accumulator (kept rows), 0 (skipped rows)
+ * Phases that do not apply to a dtype (the float32 path has one kernel pass,
+ * run by LF_BWD_MAIN) enqueue nothing.  An empty or unknown mask is
+ * LF_EINVAL.
+ */
+#define LF_BWD_PREPARE 1u
+#define LF_BWD_MAIN 2u
+#define LF_BWD_FINALIZE 4u
+#define LF_BWD_ALL 7u
+lf_status lf_attn_bwd_phases(const lf_shape* shape, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dout, const float* D,
+                             const int32_t* kept_idx, const int32_t* kept_count,
+                             const float* block_w, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, uint32_t phases,
+                             void* stream);
+
 /* Bytes of device workspace lf_attn_bwd needs for `shape` (0 if the shape is
  * invalid).  Currently the float32 dq accumulator: B*Hq*N*d*4 bytes. */
 size_t lf_bwd_workspace_bytes(const lf_shape* shape);

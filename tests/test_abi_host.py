@@ -135,3 +135,18 @@ def test_binding_rejects_unsupported_dtype():
     import torch
     with pytest.raises(bd.LazyFlashError):
         bd.make_shape(1, 1, 1, 64, 64, 64, True, 0.1, torch.float16)
+
+
+def test_bwd_phase_mask_checked():
+    lib = bd.load()
+    shp = _shape()
+
+    def call(mask):
+        return lib.lf_attn_bwd_phases(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0, mask, NULL)
+    assert call(0) == bd.LF_EINVAL
+    assert call(8) == bd.LF_EINVAL
+    assert b"phase" in lib.lf_last_error()
+    # a valid mask reaches the workspace check
+    assert call(bd.BWD_MAIN) == bd.LF_EINVAL
+    assert b"workspace" in lib.lf_last_error()
