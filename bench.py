@@ -85,15 +85,12 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    shp = bd.make_shape(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d, cfg.block, cfg.causal, cfg.scale,
-                        cfg.torch_dtype)
-    ws = torch.empty(max(bd.bwd_workspace_bytes(shp), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def run_steps(delta, seeds):
         """Runs one step per seed; returns per-step event pairs and selections."""
         sels = [bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev) for _ in seeds]
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in seeds]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in seeds]
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         for seed, sel, ev in zip(seeds, sels, evs):
@@ -103,17 +100,14 @@ def main():
             bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
                             scale=cfg.scale, heads_kv=cfg.Hkv, out=sel)
             ev[2].record(stream)
-            common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, workspace=ws,
-                          out=(dq, dk, dv))
-            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_PREPARE, **common)
+            common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv))
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DKDV, **common)
             ev[3].record(stream)
-            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_MAIN, **common)
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DQ, **common)
             ev[4].record(stream)
-            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_FINALIZE, **common)
-            ev[5].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(5)] for e in evs])
+        ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
         flops = [metrics.bwd_flops_kept(s["block_w"].cpu().numpy(), cfg.N, cfg.d, cfg.block,
                                         cfg.causal) for s in sels]
         kept = [float((s["block_w"] != 0).float().mean().item()) for s in sels]
@@ -126,14 +120,14 @@ def main():
     run_steps(main_delta, list(range(10_000, 10_000 + args.warmup)))
     log(f"[bench] timing {args.steps} steps, delta={main_delta}")
     wall, ms, flops, kept = run_steps(main_delta, list(range(args.steps)))
-    # columns: fwd, select, bwd prepare, bwd main, bwd finalize
-    t_fwd, t_sel, t_prep, t_main, t_fin = ms.mean(axis=0)
-    t_bwd = t_prep + t_main + t_fin
+    # columns: fwd, select, bwd dK/dV walk, bwd dQ walk
+    t_fwd, t_sel, t_kv, t_q = ms.mean(axis=0)
+    t_bwd = t_kv + t_q
     t_attn_bwd = t_sel + t_bwd
     per_step_attn = ms[:, 1:].sum(axis=1)
     value = F_dense / (t_attn_bwd * 1e-3) / 1e12
     log(f"[bench] fwd {t_fwd:.3f} ms, select {t_sel:.3f} ms, bwd {t_bwd:.3f} ms "
-        f"(main {t_main:.3f}), kept {kept.mean():.4f}")
+        f"(dK/dV {t_kv:.3f}, dQ {t_q:.3f}), kept {kept.mean():.4f}")
 
     sweep = {}
     for dl in cfg.deltas:
@@ -159,14 +153,19 @@ def main():
             eff_tflops=round(F_dense / (attn_ms * 1e-3) / 1e12, 2),
             kept_fraction=round(float(kept_d.mean()), 5),
             kept_work_fraction=round(float(fl_d.mean() / F_dense), 5),
-            main_kernel_tflops_on_kept=round(float(fl_d.sum() / (ms_d[:, 3].sum() * 1e-3) / 1e12), 2),
+            bwd_tflops_on_kept=round(float(fl_d.sum() / (ms_d[:, 2:].sum() * 1e-3) / 1e12), 2),
+            dkdv_ms=round(float(ms_d[:, 2].mean()), 4), dq_ms=round(float(ms_d[:, 3].mean()), 4),
         ))
     dense_ms = next((s["attn_bwd_ms"] for s in sweep_out if s["delta"] == 0.0), None)
     speedup = round(dense_ms / t_attn_bwd, 3) if dense_ms else None
 
-    # roofline of the dominant kernel of the measured region: the backward walk
-    achieved = float(flops.sum() / (ms[:, 3].sum() * 1e-3) / 1e12)
+    # Roofline of the measured region's dominant work, the backward walks.  The
+    # algorithmic work is the five products over the unmasked pairs of kept
+    # blocks (F_kept); the dK/dV walk does four of them (8 d FLOP per pair),
+    # the dQ walk recomputes S and dP and does dS K (6 d FLOP per pair), so the
+    # algorithmic rate of the pair of launches is F_kept / (t_dkdv + t_dq).
     peak = metrics.MI355X_PEAK["bf16_flops"] / 1e12
+    achieved = float(flops.sum() / (ms[:, 2:].sum() * 1e-3) / 1e12)
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
         prof = json.load(open(PROFILE_TRAFFIC))
@@ -175,8 +174,11 @@ def main():
             traffic = prof.get("bytes_per_launch")
     roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=peak, unit="TFLOP/s",
                     frac=round(achieved / peak, 4), traffic=traffic,
-                    kernel="bwd_bf16_kernel (backward tile walk over kept blocks)",
-                    algorithmic_flops_per_launch=float(flops.mean()))
+                    kernel="dkdv_bf16_kernel + dq_bf16_kernel (backward walks over kept blocks)",
+                    algorithmic_flops_per_launch=float(flops.mean()),
+                    executed_mfma_flops_per_launch=float(flops.mean() * 1.4),
+                    dkdv_tflops=round(float(0.8 * flops.sum() / (ms[:, 2].sum() * 1e-3) / 1e12), 2),
+                    dq_tflops_executed=round(float(0.6 * flops.sum() / (ms[:, 3].sum() * 1e-3) / 1e12), 2))
     others = dict(
         fwd=dict(bound="mfma", achieved=round(F_fwd / (t_fwd * 1e-3) / 1e12, 2), peak=peak,
                  unit="TFLOP/s"),
@@ -218,8 +220,7 @@ def main():
         "attn_bwd_ms_max": round(float(per_step_attn.max()), 4),
         "select_ms": round(t_sel, 4),
         "bwd_ms": round(t_bwd, 4),
-        "bwd_phases_ms": {"prepare": round(t_prep, 4), "main": round(t_main, 4),
-                          "finalize": round(t_fin, 4)},
+        "bwd_phases_ms": {"dkdv": round(t_kv, 4), "dq": round(t_q, 4)},
         "fwd_ms": round(t_fwd, 4),
         "kept_fraction": round(float(kept.mean()), 5),
         "kept_work_fraction": round(float(flops.mean() / F_dense), 5),

@@ -1,8 +1,8 @@
 """ctypes binding of liblazyflash.so (C ABI in include/lazyflash.h).
 
 Argument marshalling only: every step of the computation runs in the HIP
-library.  torch provides device memory (outputs and the backward workspace are
-allocated here as torch tensors) and the current HIP stream.  The library is
+library.  torch provides device memory (outputs are allocated here as torch
+tensors) and the current HIP stream.  The library is
 loaded from this package directory; if it is missing the import of any entry
 point raises, there is no fallback.
 """
@@ -12,15 +12,15 @@ import os
 import torch
 
 __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block_select",
-           "select_outputs", "attn_bwd", "bwd_workspace_bytes", "EXPORTED_SYMBOLS", "LIB_PATH"]
+           "select_outputs", "attn_bwd", "EXPORTED_SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
 EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_attn_bwd_phases",
-                    "lf_bwd_workspace_bytes", "lf_status_str", "lf_last_error", "lf_abi_version")
-BWD_PREPARE, BWD_MAIN, BWD_FINALIZE, BWD_ALL = 1, 2, 4, 7
+                    "lf_status_str", "lf_last_error", "lf_abi_version")
+BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 3
 
 
 class LazyFlashError(RuntimeError):
@@ -55,13 +55,10 @@ def load(path=LIB_PATH):
     lib.lf_attn_fwd.restype = I32
     lib.lf_block_select.argtypes = [S, P, P, D, U64, P, P, P, P, P, P, P]
     lib.lf_block_select.restype = I32
-    lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.lf_attn_bwd.restype = I32
-    lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z,
-                                       ctypes.c_uint32, P]
+    lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, P]
     lib.lf_attn_bwd_phases.restype = I32
-    lib.lf_bwd_workspace_bytes.argtypes = [S]
-    lib.lf_bwd_workspace_bytes.restype = Z
     lib.lf_status_str.argtypes = [I32]
     lib.lf_status_str.restype = ctypes.c_char_p
     lib.lf_last_error.argtypes = []
@@ -178,16 +175,11 @@ def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads
     return out
 
 
-def bwd_workspace_bytes(shape):
-    return int(load().lf_bwd_workspace_bytes(ctypes.byref(shape)))
-
-
-def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, workspace=None,
-             out=None, phases=BWD_ALL):
+def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=None,
+             phases=BWD_ALL):
     """Sparse backward over the kept blocks of `sel` (the dict of block_select).
-    Returns (dq, dk, dv).  `workspace` (uint8 device tensor) and `out`
-    (preallocated (dq, dk, dv)) are optional; `phases` selects a subset of the
-    backward's phases (see lf_attn_bwd_phases)."""
+    Returns (dq, dk, dv).  `out` optionally gives preallocated (dq, dk, dv);
+    `phases` selects the dK/dV walk, the dQ walk, or both."""
     lib = load()
     shp, _ = _shape_from(q, k, block, causal, scale)
     dev = q.device
@@ -201,9 +193,6 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, worksp
     _need(sel["kept_idx"], "kept_idx", (B, Hq, nqb), torch.int32, dev)
     _need(sel["kept_count"], "kept_count", (B, Hq), torch.int32, dev)
     _need(sel["block_w"], "block_w", (B, Hq, nqb), torch.float32, dev)
-    need = int(lib.lf_bwd_workspace_bytes(ctypes.byref(shp)))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = out
@@ -212,7 +201,7 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, worksp
     _need(dv, "dv", k.shape, q.dtype, dev)
     args = (ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(sel["D"]),
             _ptr(sel["kept_idx"]), _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq),
-            _ptr(dk), _ptr(dv), _ptr(workspace), ctypes.c_size_t(workspace.numel()))
+            _ptr(dk), _ptr(dv))
     if phases == BWD_ALL:
         _check(lib, lib.lf_attn_bwd(*args, _stream(dev)))
     else:

@@ -82,14 +82,6 @@ const char* lf_last_error(void) { return g_err; }
 
 int32_t lf_abi_version(void) { return LF_ABI_VERSION; }
 
-size_t lf_bwd_workspace_bytes(const lf_shape* s) {
-    lf::Problem pb;
-    bool empty;
-    if (check_shape(s, pb, empty) != LF_OK) return 0;
-    if (!pb.bf16 || empty) return 0;
-    return (size_t)pb.B * pb.Hq * pb.N * pb.d * sizeof(float);
-}
-
 lf_status lf_attn_fwd(const lf_shape* s, const void* q, const void* k, const void* v, void* o,
                       float* lse, void* stream) {
     lf::Problem pb;
@@ -119,8 +111,7 @@ lf_status lf_block_select(const lf_shape* s, const void* o, const void* dout, do
 lf_status lf_attn_bwd_phases(const lf_shape* s, const void* q, const void* k, const void* v,
                              const float* lse, const void* dout, const float* D,
                              const int32_t* kept_idx, const int32_t* kept_count,
-                             const float* block_w, void* dq, void* dk, void* dv,
-                             void* workspace, size_t workspace_bytes, uint32_t phases,
+                             const float* block_w, void* dq, void* dk, void* dv, uint32_t phases,
                              void* stream) {
     lf::Problem pb;
     bool empty;
@@ -128,23 +119,19 @@ lf_status lf_attn_bwd_phases(const lf_shape* s, const void* q, const void* k, co
     if (st != LF_OK) return st;
     if (phases == 0 || (phases & ~LF_BWD_ALL) != 0) return fail(LF_EINVAL, "bad phase mask");
     if (empty) return hip_status(hipSuccess);
-    if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv}))
+    if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w}) ||
+        ((phases & LF_BWD_DQ) && !dq) || ((phases & LF_BWD_DKDV) && (!dk || !dv)))
         return fail(LF_EINVAL, "NULL tensor pointer");
-    const size_t need = lf_bwd_workspace_bytes(s);
-    if (need && (!workspace || workspace_bytes < need))
-        return fail(LF_EINVAL, "workspace missing or smaller than lf_bwd_workspace_bytes()");
     return hip_status(lf::launch_bwd(pb, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq,
-                                     dk, dv, static_cast<float*>(workspace), phases,
-                                     (hipStream_t)stream));
+                                     dk, dv, phases, (hipStream_t)stream));
 }
 
 lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* dq, void* dk, void* dv, void* stream) {
     return lf_attn_bwd_phases(s, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv,
-                              workspace, workspace_bytes, LF_BWD_ALL, stream);
+                              LF_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -13,30 +13,39 @@
 //   dV = sum_i w_i P_i^T dO_i,   dK = scale sum_i w_i dS_i^T Q_i,
 //   dQ_i = w_i scale dS_i K            (rows of skipped blocks: 0).
 // The weight is folded into the exponent: exp2(s - (LSE log2 e - log2 w)) =
-// w P, so dS and the dV/dK/dQ products carry it for free.
+// w P, so dS and every product carry it for free.
 //
-// bf16 kernel (gfx950): one workgroup of 4 waves per (batch, kv head, 128-key
-// tile); wave w owns keys 32w..32w+31 and keeps its K/V fragments and its
-// dK/dV accumulators in registers for the whole walk.  The workgroup walks the
-// kept blocks of the Hq/Hkv query heads of its group in 64-row sub-tiles
-// (Q, dO, LSE', D staged in LDS) and per sub-tile does, on 32x32x16 MFMAs:
-//   S = Q K_w^T and dP = dO V_w^T (A from LDS rows, B in registers),
-//   dV_w += P^T dO and dK_w += dS^T Q (A = P / dS straight from the score
-//   accumulators, B from transposing LDS reads of the row-major tiles),
-//   dQ_tile = dS K (dS^T through LDS, K^T fragments in registers), added with
-//   float atomics into an fp32 workspace; a last pass scales and converts it.
-// Skipped blocks never enter the loop, so their tiles are never read.
+// Two kernels, both deterministic (no atomics, no workspace):
+//
+// dkdv_bf16_kernel -- one workgroup of 4 waves per (batch, kv head, 128-key
+//   tile); wave w owns keys 32w..32w+31 and keeps its K/V fragments and its
+//   dK/dV accumulators in registers for the whole walk.  The workgroup walks
+//   the kept blocks of the Hq/Hkv query heads of its group in 64-row
+//   sub-tiles; Q and dO rows go from HBM straight into double-buffered LDS
+//   (buffer loads to LDS) while the previous sub-tile computes.  Per sub-tile,
+//   on 32x32x16 bf16 MFMAs: S = Q K_w^T and dP = dO V_w^T (A: LDS rows, B:
+//   registers), P' and dS' in the accumulator layout, then dV_w += P'^T dO and
+//   dK_w += dS'^T Q (A: P' / dS' straight from the score accumulators, B:
+//   transposing LDS reads of the row-major tiles).
+//
+// dq_bf16_kernel -- one workgroup per query block (skipped blocks just write
+//   their zero rows); each wave owns 32 query rows, keeps Q and dO fragments,
+//   its LSE'/D row terms and its dQ accumulator in registers, and walks the
+//   64-key tiles it can see, staged in double-buffered LDS.  Scores are
+//   computed transposed, S^T = K Q^T and dP^T = V dO^T, so dS^T in the
+//   accumulator layout is directly the A operand of dQ += dS K; K^T comes from
+//   transposing LDS reads.  Small enough for two waves per SIMD.
 #include "lf_common.h"
 #include "lf_internal.h"
 
 namespace lf {
 
-constexpr int kBN = 128;  // keys per workgroup
-constexpr int kBM = 64;   // query rows per sub-tile
-constexpr int kBPad = 8;
+constexpr int kBN = 128;  // keys per dK/dV workgroup
+constexpr int kBM = 64;   // query rows per dK/dV sub-tile
+constexpr int kQN = 64;   // keys per dQ step
+constexpr int kBPad = 8;  // bf16 elements of padding per LDS row
 
-__device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int nkt, int& b, int& g,
-                                              int& j) {
+__device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int& b, int& g, int& j) {
     const int nG = B * Hkv;
     int gid;
     if (nG % kNumXcd == 0) {
@@ -50,54 +59,233 @@ __device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int nkt, 
     }
     b = gid / Hkv;
     g = gid % Hkv;
-    (void)nkt;
 }
 
-// first position in the ascending list with value >= x
-__device__ __forceinline__ int lower_bound_i32(const int32_t* list, int n, int x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (list[mid] < x) lo = mid + 1;
-        else hi = mid;
+// Workgroup -> (batch, query head, query block): heads of one kv group on one
+// XCD, largest causal blocks first.
+__device__ __forceinline__ void map_dq_block(int bid, int B, int Hq, int Hkv, int nqb, bool causal,
+                                             int& b, int& h, int& i) {
+    const int G = Hq / Hkv;
+    const int nG = B * Hkv;
+    int tr;
+    if (nG % kNumXcd == 0) {
+        const int xcd = bid % kNumXcd, r = bid / kNumXcd;
+        const int nhx = (nG / kNumXcd) * G;
+        const int hi = r % nhx;
+        tr = r / nhx;
+        const int gid = xcd + kNumXcd * (hi / G);
+        b = gid / Hkv;
+        h = (gid % Hkv) * G + hi % G;
+    } else {
+        const int hi = bid % (B * Hq);
+        tr = bid / (B * Hq);
+        b = hi / Hq;
+        h = hi % Hq;
     }
-    return lo;
+    i = causal ? nqb - 1 - tr : tr;
 }
+
+// LDS tiles are row-major [ROWS][HD] bf16 with no padding; the 16-byte chunk c
+// of row r is stored at chunk position c ^ swz(r).  With this map both reads
+// the kernels make are free of bank conflicts (64 banks of 4 bytes): a
+// 32x32x16 operand fragment (16 lanes reading one chunk of 16 consecutive
+// rows) and a transposing read (32 lanes reading 4 consecutive chunks of 4
+// consecutive rows, rows starting at a multiple of 4).
+template <int HD>
+__device__ __forceinline__ constexpr int swz(int r) {
+    return HD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Loads a swizzled [ROWS][HD] bf16 tile straight from HBM into LDS with 16-byte
+// buffer loads: lane l of a wave-instruction writes LDS bytes [16 l, 16 l + 16)
+// after the instruction's base, so slot S = 64 m + l is chunk position S % CPR
+// of row S / CPR, and the lane fetches the logical chunk that belongs there.
+// `soff` is the byte offset of the tile's first row inside the buffer `rs`.
+template <int HD, int ROWS, int NWAVES>
+__device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t rs, int soff, bf16* lds,
+                                                 int wave, int lane) {
+    constexpr int CPR = HD / 8;
+    constexpr int NINST = ROWS * CPR / 64;
+    static_assert(ROWS * CPR % 64 == 0, "slot layout");
+    for (int m = wave; m < NINST; m += NWAVES) {
+        const int S = 64 * m + lane;
+        const int row = S / CPR, c = (S % CPR) ^ swz<HD>(S / CPR);
+        const int voff = (row * HD + c * 8) * (int)sizeof(bf16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * m), 16, voff, soff, 0, 0);
+    }
+}
+
+// Per-lane byte offsets into a swizzled tile, fixed for the kernel's life:
+//   frag[ks]    32x32x16 operand fragment of row (R + l32), head-dim chunk
+//               2 ks + hf, for any R that is a multiple of 16;
+//   tr[dt][s]   transposing read of rows R + 4 hf + (j16 >> 2) + 8 s, columns
+//               32 dt + 16 (G16 & 1) + 4 (j16 & 3) .. +3, R a multiple of 16.
+// R * HD * 2 is then an immediate offset of the LDS instruction.
+template <int HD>
+struct TileOffsets {
+    int frag[HD / 16];
+    int tr[HD / 32][2];
+    __device__ __forceinline__ TileOffsets(int lane) {
+        const int l32 = lane & 31, hf = lane >> 5, G16 = lane >> 4, j16 = lane & 15;
+        constexpr int rowB = HD * 2;
+#pragma unroll
+        for (int ks = 0; ks < HD / 16; ++ks)
+            frag[ks] = l32 * rowB + 16 * ((2 * ks + hf) ^ swz<HD>(l32));
+#pragma unroll
+        for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int r = 4 * hf + (j16 >> 2) + 8 * s;
+                const int c = 4 * dt + 2 * (G16 & 1) + ((j16 >> 1) & 1);
+                tr[dt][s] = r * rowB + 16 * (c ^ swz<HD>(r)) + 8 * (j16 & 1);
+            }
+    }
+};
+
+template <int HD>
+__device__ __forceinline__ bf16x8 frag_at(const bf16* tile, int R, int off) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + R * HD * 2 + off);
+}
+template <int HD>
+__device__ __forceinline__ bf16x8 tr_at(const bf16* tile, int R, const int (&off)[2]) {
+    const char* t = reinterpret_cast<const char*>(tile) + R * HD * 2;
+    return cat(lds_read_tr(reinterpret_cast<const bf16*>(t + off[0])),
+               lds_read_tr(reinterpret_cast<const bf16*>(t + off[1])));
+}
+
+// Scheduling hint for a block of NR LDS reads feeding NM MFMAs: issue AHEAD
+// reads first, then alternate one MFMA with PER reads, then the last MFMAs.
+// (Only orders instructions already in the scheduling region.)
+template <int NR, int NM, int PER, int AHEAD>
+__device__ __forceinline__ void pipeline_schedule() {
+    constexpr int kDsRead = 0x100, kMfma = 0x008;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD, 0);
+    constexpr int rest = NR - AHEAD;
+    constexpr int steps = rest / PER;
+#pragma unroll
+    for (int i = 0; i < steps; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, PER, 0);
+    }
+    if (rest % PER) __builtin_amdgcn_sched_group_barrier(kDsRead, rest % PER, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, NM - steps, 0);
+}
+
+// Walk over the work of one workgroup: the heads of its group, their kept
+// blocks in ascending order, and the 64-row sub-tiles of each block that reach
+// the workgroup's keys under the causal mask.  The walk position is uniform
+// (scalar registers); the kept list is read 64 entries at a time into one
+// vector register per wave (entry pos - cbase in lane pos - cbase), together
+// with log2 of each entry's weight, and looked up with v_readlane, so moving
+// to the next sub-tile costs no memory round trip.
+template <int BLK, bool CAUSAL>
+struct Walk {
+    const int32_t* kept_idx;
+    const int32_t* kept_count;
+    const float* block_w;
+    int Hq, nqb, G, b, g, k0, lane;
+    int hg, cnt, pos, st, i, bh, cbase;
+    float lw;
+    int vidx;    // kept_idx[bh][cbase + lane]  (or a large sentinel past cnt)
+    float vlw;   // log2(block_w[bh][vidx])
+
+    __device__ __forceinline__ void load_chunk(int c) {
+        cbase = c;
+        const int p = c + lane;
+        int idx = 0x7fffffff;
+        float w = 1.f;
+        if (p < cnt) {
+            idx = kept_idx[(size_t)bh * nqb + p];
+            if ((unsigned)idx < (unsigned)nqb) w = block_w[(size_t)bh * nqb + idx];
+        }
+        vidx = idx;
+        vlw = __log2f(w);
+    }
+    __device__ __forceinline__ void load_head() {
+        bh = b * Hq + g * G + hg;
+        cnt = min(max(kept_count[bh], 0), nqb);
+        st = 0;
+        pos = cnt;
+        // first kept block whose rows reach key k0 (all of them when not causal)
+        const int first_block = CAUSAL ? k0 / BLK : 0;
+        for (int c = 0; c < cnt; c += 64) {
+            load_chunk(c);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(vidx >= first_block);
+            if (m) {
+                pos = c + __builtin_ctzll(m);
+                break;
+            }
+        }
+    }
+    // advance until (hg, pos, st) names a valid sub-tile; false when none is left
+    __device__ __forceinline__ bool settle() {
+        while (true) {
+            if (pos >= cnt) {
+                if (++hg >= G) return false;
+                load_head();
+                continue;
+            }
+            if (pos - cbase >= 64) load_chunk(pos & ~63);
+            i = __builtin_amdgcn_readlane(vidx, pos - cbase);
+            if ((unsigned)i >= (unsigned)nqb || st >= BLK / kBM) {  // malformed entry or block done
+                ++pos;
+                st = 0;
+                continue;
+            }
+            if (CAUSAL && i * BLK + st * kBM + kBM - 1 < k0) {  // rows all before the keys
+                ++st;
+                continue;
+            }
+            lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                               __builtin_bit_cast(int, vlw), pos - cbase));
+            return true;
+        }
+    }
+    __device__ __forceinline__ bool first() {
+        hg = 0;
+        load_head();
+        return settle();
+    }
+    __device__ __forceinline__ bool next() {
+        ++st;
+        return settle();
+    }
+    __device__ __forceinline__ int q0() const { return i * BLK + st * kBM; }
+};
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 template <int HD, int BLK, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_bf16_kernel(
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ Drow,
     const int32_t* __restrict__ kept_idx, const int32_t* __restrict__ kept_count,
-    const float* __restrict__ block_w, bf16* __restrict__ dk, bf16* __restrict__ dv,
-    float* __restrict__ dq_acc, int B, int Hq, int Hkv, int N, int nqb, float scale,
-    float scale_log2) {
+    const float* __restrict__ block_w, bf16* __restrict__ dk, bf16* __restrict__ dv, int B, int Hq,
+    int Hkv, int N, int nqb, float scale, float scale_log2) {
     constexpr int KS = HD / 16;        // k-steps over the head dim
     constexpr int DT = HD / 32;        // 32-wide head-dim tiles
-    constexpr int LD = HD + kBPad;     // row stride of sQ / sdO / sK
-    constexpr int LDT = kBM + kBPad;   // row stride of sdsT (q contiguous)
-    constexpr int CH = kBM * HD / 8;   // 16-byte chunks per staged tile
-    constexpr int CPT = CH / 256;
+    constexpr int TILE = kBM * HD;     // one staged Q or dO tile (swizzled)
 
-    __shared__ __attribute__((aligned(16))) bf16 sQ[kBM * LD];
-    __shared__ __attribute__((aligned(16))) bf16 sdO[kBM * LD];
-    __shared__ __attribute__((aligned(16))) bf16 sdsT[kBN * LDT];
-    __shared__ __attribute__((aligned(16))) float sLse[kBM];
-    __shared__ __attribute__((aligned(16))) float sD[kBM];
+    // double-buffered staging: [buffer][Q | dO], LSE' | D per buffer
+    __shared__ __attribute__((aligned(16))) bf16 sQD[2][2][TILE];
+    __shared__ __attribute__((aligned(16))) float sLD[2][2][kBM];
 
-    const int nkt = (N + kBN - 1) / kBN;
     int b, g, j;
-    map_bwd_block(blockIdx.x, B, Hkv, nkt, b, g, j);
+    map_bwd_block(blockIdx.x, B, Hkv, b, g, j);
     const int G = Hq / Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hf = lane >> 5, G16 = lane >> 4, j16 = lane & 15;
+    const int l32 = lane & 31, hf = lane >> 5;
     const int k0 = j * kBN;
     const int key = k0 + 32 * wave + l32;  // key column held by this lane
     const bool key_ok = key < N;
-
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
+    const f32x16 zero16 = {};
+    const TileOffsets<HD> off(lane);
 
-    // K and V fragments (B operands of S = Q K^T, dP = dO V^T)
+    // ---- K and V fragments: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[KS], vf[KS];
     {
         const size_t r = kvoff + (size_t)(key_ok ? key : 0) * HD;
@@ -108,108 +296,97 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
             if (!key_ok) { kf[ks] = bf16x8{}; vf[ks] = bf16x8{}; }
         }
     }
-    // K^T fragments for dQ = dS K: B[k = key, n = d], this wave's d tile.
-    // Staged once through LDS (sQ/sdO hold the 128 x HD K tile here).
-    constexpr int QT_DQ = (HD == 128) ? 2 : 1;   // q tiles per wave in dQ
-    const int dq_d0 = (HD == 128) ? 32 * wave : 32 * (wave & 1);
-    const int dq_qt0 = (HD == 128) ? 0 : (wave >> 1);
-    bf16x8 ktf[kBN / 16];
-    {
-        // rows 0..63 of the K tile go to sQ, rows 64..127 to sdO
-        for (int c = tid; c < kBN * HD / 8; c += 256) {
-            const int row = c / (HD / 8), col = (c % (HD / 8)) * 8;
-            const int kk = k0 + row;
-            u32x4 val = u32x4{};
-            if (kk < N) val = *reinterpret_cast<const u32x4*>(k + kvoff + (size_t)kk * HD + col);
-            bf16* dst = (row < kBM) ? &sQ[row * LD + col] : &sdO[(row - kBM) * LD + col];
-            *reinterpret_cast<u32x4*>(dst) = val;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < kBN / 16; ++ks) {
-            const int r0 = 16 * ks + 8 * hf + (j16 >> 2);
-            const int col = dq_d0 + 16 * (G16 & 1) + 4 * (j16 & 3);
-            const bf16* p0 = (r0 < kBM) ? &sQ[r0 * LD + col] : &sdO[(r0 - kBM) * LD + col];
-            const int r1 = r0 + 4;
-            const bf16* p1 = (r1 < kBM) ? &sQ[r1 * LD + col] : &sdO[(r1 - kBM) * LD + col];
-            ktf[ks] = cat(lds_read_tr(p0), lds_read_tr(p1));
-        }
-        __syncthreads();
-    }
 
     f32x16 acc_dk[DT], acc_dv[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) { acc_dk[dt] = f32x16{}; acc_dv[dt] = f32x16{}; }
+    for (int dt = 0; dt < DT; ++dt) { acc_dk[dt] = zero16; acc_dv[dt] = zero16; }
 
-    for (int hg = 0; hg < G; ++hg) {
-        const int h = g * G + hg;
-        const int bh = b * Hq + h;
-        const int cnt = min(max(kept_count[bh], 0), nqb);
-        const int32_t* list = kept_idx + (size_t)bh * nqb;
-        const int start = CAUSAL ? lower_bound_i32(list, cnt, k0 / BLK) : 0;
-        const size_t qoff = (size_t)bh * (size_t)N * HD;
-        for (int pos = start; pos < cnt; ++pos) {
-            const int i = list[pos];
-            if ((unsigned)i >= (unsigned)nqb) continue;  // malformed list: skip
-            const float lw = __log2f(block_w[(size_t)bh * nqb + i]);
-#pragma unroll 1
-            for (int st = 0; st < BLK / kBM; ++st) {
-                const int qs0 = i * BLK + st * kBM;
-                if (CAUSAL && qs0 + kBM - 1 < k0) continue;
-                // ---- stage Q, dO rows, LSE' and D
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) {
-                    const int chunk = tid + 256 * c;
-                    const int row = chunk / (HD / 8), col = (chunk % (HD / 8)) * 8;
-                    const size_t src = qoff + (size_t)(qs0 + row) * HD + col;
-                    *reinterpret_cast<u32x4*>(&sQ[row * LD + col]) =
-                        *reinterpret_cast<const u32x4*>(q + src);
-                    *reinterpret_cast<u32x4*>(&sdO[row * LD + col]) =
-                        *reinterpret_cast<const u32x4*>(dout + src);
-                }
-                if (tid < kBM) {
-                    sLse[tid] = lse[(size_t)bh * N + qs0 + tid] * kLog2e - lw;
-                } else if (tid < 2 * kBM) {
-                    sD[tid - kBM] = Drow[(size_t)bh * N + qs0 + tid - kBM];
-                }
-                __syncthreads();
+    Walk<BLK, CAUSAL> W;
+    W.kept_idx = kept_idx;
+    W.kept_count = kept_count;
+    W.block_w = block_w;
+    W.lane = lane;
+    W.Hq = Hq;
+    W.nqb = nqb;
+    W.G = G;
+    W.b = b;
+    W.g = g;
+    W.k0 = k0;
 
-                // ---- S = Q K_w^T, dP = dO V_w^T   (rows = q, cols = keys)
-                f32x16 s[2], dp[2];
+    // A sub-tile's Q and dO rows go straight to LDS; LSE' and D take a
+    // one-register path (they are transformed on the way).
+    float pld = 0.f;
+    const uint32_t head_bytes = (uint32_t)N * HD * sizeof(bf16);
+    auto fetch = [&](int bh, int qs0, float lw, int BF) {
+        const size_t hoff = (size_t)bh * N * HD;
+        const int soff = qs0 * HD * (int)sizeof(bf16);
+        load_tile_to_lds<HD, kBM, 4>(make_rsrc(q + hoff, head_bytes), soff, sQD[BF][0], wave, lane);
+        load_tile_to_lds<HD, kBM, 4>(make_rsrc(dout + hoff, head_bytes), soff, sQD[BF][1], wave,
+                                     lane);
+        if (tid < kBM) pld = lse[(size_t)bh * N + qs0 + tid] * kLog2e - lw;
+        else if (tid < 2 * kBM) pld = Drow[(size_t)bh * N + qs0 + tid - kBM];
+    };
+    auto stage = [&](int BF) {
+        if (tid < 2 * kBM) sLD[BF][tid / kBM][tid % kBM] = pld;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    if (W.first()) {
+        int cur_bh = W.bh, cur_q0 = W.q0();
+        float cur_lw = W.lw;
+        fetch(cur_bh, cur_q0, cur_lw, 0);
+        stage(0);
+        __syncthreads();
+
+        // One sub-tile, one 32-row query tile at a time: S and dP, then P' and
+        // dS' in the accumulator layout, then the dV/dK k-steps over those rows.
+        auto body = [&](int BUF, bool mask) {
+            // element (query row ql, this lane's key) is kept iff ql >= thr:
+            // causal needs key <= cur_q0 + ql; keys past N are never kept
+            const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
+            const bf16* sq = sQD[BUF][0];
+            const bf16* sdo = sQD[BUF][1];
+            const float* sl = sLD[BUF][0];
+            const float* sd = sLD[BUF][1];
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    s[qt] = f32x16{};
-                    dp[qt] = f32x16{};
-                    const bf16* qa = &sQ[(32 * qt + l32) * LD + 8 * hf];
-                    const bf16* oa = &sdO[(32 * qt + l32) * LD + 8 * hf];
+            for (int qt = 0; qt < 2; ++qt) {
+                f32x16 s, dp;
+                {
+                    bf16x8 aq[KS], ao[KS];
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        s[qt] = mfma32(*reinterpret_cast<const bf16x8*>(qa + 16 * ks), kf[ks], s[qt]);
-                        dp[qt] = mfma32(*reinterpret_cast<const bf16x8*>(oa + 16 * ks), vf[ks], dp[qt]);
+                        aq[ks] = frag_at<HD>(sq, 32 * qt, off.frag[ks]);
+                        ao[ks] = frag_at<HD>(sdo, 32 * qt, off.frag[ks]);
                     }
-                }
-                // ---- P' = w P and dS' = w dS, in the accumulator layout
-                const bool need_mask = (CAUSAL && k0 + kBN - 1 > qs0) || (k0 + kBN > N);
-                bf16x8 pa[4], da[4];
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    float pv[16], dv_[16];
+                    for (int ks = 0; ks < KS; ++ks) {
+                        s = mfma32(aq[ks], kf[ks], ks ? s : zero16);
+                        dp = mfma32(ao[ks], vf[ks], ks ? dp : zero16);
+                    }
+                    pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 pa[2], da[2];
+                {
+                    float pv[16], dsv[16];
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
-                        const int ql = 32 * qt + 8 * a + 4 * hf;
-                        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sLse[ql]);
-                        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[ql]);
+                        const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a + 4 * hf);
 #pragma unroll
-                        for (int bb = 0; bb < 4; ++bb) {
-                            const int r = 4 * a + bb;
-                            float p = fast_exp2(s[qt][r] * scale_log2 - L4[bb]);
-                            if (need_mask) {
-                                const int qg = qs0 + ql + bb;
-                                if (!key_ok || (CAUSAL && key > qg)) p = 0.f;
-                            }
-                            pv[r] = p;
-                            dv_[r] = p * (dp[qt][r] - D4[bb]);
-                        }
+                        for (int bb = 0; bb < 4; ++bb)
+                            pv[4 * a + bb] = fast_exp2(s[4 * a + bb] * scale_log2 - L4[bb]);
+                    }
+                    if (mask) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (32 * qt + 8 * (r >> 2) + (r & 3) < thr) pv[r] = 0.f;
+                    }
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const f32x4 D4 = *reinterpret_cast<const f32x4*>(sd + 32 * qt + 8 * a + 4 * hf);
+#pragma unroll
+                        for (int bb = 0; bb < 4; ++bb)
+                            dsv[4 * a + bb] = pv[4 * a + bb] * (dp[4 * a + bb] - D4[bb]);
                     }
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
@@ -217,109 +394,240 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             fp[e] = to_bf16(pv[8 * half + e]);
-                            fd[e] = to_bf16(dv_[8 * half + e]);
+                            fd[e] = to_bf16(dsv[8 * half + e]);
                         }
-                        pa[2 * qt + half] = fp;
-                        da[2 * qt + half] = fd;
-                    }
-                    // dS^T to LDS: key row (32w + l32), 4 consecutive q per store
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        bf16x4 w4;
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb) w4[bb] = to_bf16(dv_[4 * a + bb]);
-                        *reinterpret_cast<bf16x4*>(
-                            &sdsT[(32 * wave + l32) * LDT + 32 * qt + 8 * a + 4 * hf]) = w4;
+                        pa[half] = fp;
+                        da[half] = fd;
                     }
                 }
-                // ---- dV_w += P'^T dO, dK_w += dS'^T Q   (B via transposing reads)
+                // dV_w += P'^T dO, dK_w += dS'^T Q over these 32 query rows
+                {
+                    bf16x8 bo[2][DT], bq[2][DT];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int rb = 16 * ks + 4 * hf + (j16 >> 2);
+                    for (int half = 0; half < 2; ++half)
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const int col = 32 * dt + 16 * (G16 & 1) + 4 * (j16 & 3);
-                        const bf16x8 bo = cat(lds_read_tr(&sdO[rb * LD + col]),
-                                              lds_read_tr(&sdO[(rb + 8) * LD + col]));
-                        acc_dv[dt] = mfma32(pa[ks], bo, acc_dv[dt]);
-                        const bf16x8 bq = cat(lds_read_tr(&sQ[rb * LD + col]),
-                                              lds_read_tr(&sQ[(rb + 8) * LD + col]));
-                        acc_dk[dt] = mfma32(da[ks], bq, acc_dk[dt]);
-                    }
+                        for (int dt = 0; dt < DT; ++dt) {
+                            bo[half][dt] = tr_at<HD>(sdo, 32 * qt + 16 * half, off.tr[dt]);
+                            bq[half][dt] = tr_at<HD>(sq, 32 * qt + 16 * half, off.tr[dt]);
+                        }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) {
+                            acc_dv[dt] = mfma32(pa[half], bo[half][dt], acc_dv[dt]);
+                            acc_dk[dt] = mfma32(da[half], bq[half][dt], acc_dk[dt]);
+                        }
+                    pipeline_schedule<8 * DT, 4 * DT, 2, 8>();
                 }
-                __syncthreads();
-                // ---- dQ tile = dS' K : A = dS' via transposing reads of dS^T
-#pragma unroll
-                for (int qq = 0; qq < QT_DQ; ++qq) {
-                    const int qt = dq_qt0 + qq;
-                    f32x16 acc = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < kBN / 16; ++ks) {
-                        const int r0 = 16 * ks + 8 * hf + (j16 >> 2);
-                        const int col = 32 * qt + 16 * (G16 & 1) + 4 * (j16 & 3);
-                        const bf16x8 a = cat(lds_read_tr(&sdsT[r0 * LDT + col]),
-                                             lds_read_tr(&sdsT[(r0 + 4) * LDT + col]));
-                        acc = mfma32(a, ktf[ks], acc);
-                    }
-                    float* dst = dq_acc + qoff + (size_t)qs0 * HD + dq_d0 + l32;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int ql = 32 * qt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        atomicAdd(dst + (size_t)ql * HD, acc[r]);
-                    }
-                }
-                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
             }
+        };
+
+        int buf = 0;
+        while (true) {
+            // prefetch the next sub-tile (or reload this one when none is left)
+            const bool more = W.next();
+            const int nx_bh = more ? W.bh : cur_bh;
+            const int nx_q0 = more ? W.q0() : cur_q0;
+            const float nx_lw = more ? W.lw : cur_lw;
+            fetch(nx_bh, nx_q0, nx_lw, buf ^ 1);
+            const bool mask = (CAUSAL && k0 + kBN - 1 > cur_q0) || (k0 + kBN > N);
+            body(buf, mask);
+            stage(buf ^ 1);
+            __syncthreads();
+            if (!more) break;
+            buf ^= 1;
+            cur_bh = nx_bh;
+            cur_q0 = nx_q0;
+            cur_lw = nx_lw;
         }
     }
 
     // ---- epilogue: dK = scale * acc, dV = acc, bf16
-    const size_t out = kvoff;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = k0 + 32 * wave + 8 * (r >> 2) + 4 * hf + (r & 3);
             if (kr < N) {
-                const size_t o = out + (size_t)kr * HD + 32 * dt + l32;
+                const size_t o = kvoff + (size_t)kr * HD + 32 * dt + l32;
                 dk[o] = to_bf16(acc_dk[dt][r] * scale);
                 dv[o] = to_bf16(acc_dv[dt][r]);
             }
         }
 }
 
-// Zero the fp32 dQ accumulator rows of kept blocks (one workgroup per block).
-template <int HD, int BLK>
-__global__ __launch_bounds__(256) void dq_zero_kernel(const float* __restrict__ block_w,
-                                                      float* __restrict__ dq_acc) {
-    const size_t blk = blockIdx.x;
-    if (block_w[blk] == 0.f) return;
-    f32x4* dst = reinterpret_cast<f32x4*>(dq_acc + blk * (size_t)(BLK * HD));
-    for (int c = threadIdx.x; c < BLK * HD / 4; c += 256) dst[c] = f32x4{};
-}
+template <int HD, int BLK, bool CAUSAL>
+__global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ Drow,
+    const float* __restrict__ block_w, bf16* __restrict__ dq, int B, int Hq, int Hkv, int N,
+    int nqb, float scale, float scale_log2) {
+    // Two streams of NW waves each (32 query rows per wave) split the key
+    // steps of the block: stream 0 takes the even 64-key steps, stream 1 the
+    // odd ones; their dQ partials are added in LDS at the end (fixed order).
+    constexpr int NW = BLK / 32;
+    constexpr int KS = HD / 16;
+    constexpr int DT = HD / 32;
+    constexpr int TILE = kQN * HD;     // one staged K or V tile (swizzled)
+    static_assert(NW * 64 * DT * 16 * sizeof(float) <= sizeof(bf16) * 2 * 2 * 2 * TILE,
+                  "partial dQ of stream 1 fits in the K/V staging buffers");
+    __shared__ __attribute__((aligned(16))) bf16 sKV[2][2][2][TILE];   // [stream][buffer][K | V]
 
-// dQ = scale * accumulator for kept blocks, exact zeros for skipped blocks.
-template <int HD, int BLK>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ block_w,
-                                                         const float* __restrict__ dq_acc,
-                                                         bf16* __restrict__ dq, float scale) {
-    const size_t blk = blockIdx.x;
-    const bool kept = block_w[blk] != 0.f;
-    const f32x4* src = reinterpret_cast<const f32x4*>(dq_acc + blk * (size_t)(BLK * HD));
-    bf16x4* dst = reinterpret_cast<bf16x4*>(dq + blk * (size_t)(BLK * HD));
-    for (int c = threadIdx.x; c < BLK * HD / 4; c += 256) {
-        bf16x4 o4 = bf16x4{};
-        if (kept) {
-            const f32x4 x = src[c];
+    int b, h, i;
+    map_dq_block(blockIdx.x, B, Hq, Hkv, nqb, CAUSAL, b, h, i);
+    const int g = h / (Hq / Hkv);
+    const int bh = b * Hq + h;
+    const int tid = threadIdx.x, lane = tid & 63, wave_all = tid >> 6;
+    const int stream = wave_all / NW, wave = wave_all % NW;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const size_t qoff = (size_t)bh * N * HD;
+    bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
+
+    const float w = block_w[(size_t)bh * nqb + i];
+    if (w == 0.f) {  // skipped block: its dq rows are exact zeros
+        for (int c = tid; c < BLK * HD / 8; c += 2 * NW * 64)
+            *reinterpret_cast<u32x4*>(dq_rows + 8 * c) = u32x4{};
+        return;
+    }
+    const float lw = __log2f(w);
+    const int qw0 = i * BLK + 32 * wave;  // first row of this wave
+    const int qrow = qw0 + l32;           // query column held by this lane
+    const f32x16 zero16 = {};
+    const TileOffsets<HD> off(lane);
+
+    // Q^T and dO^T fragments (B operands): column = query, k = head dim
+    bf16x8 qf[KS], of[KS];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o4[e] = to_bf16(x[e] * scale);
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
+        of[ks] = *reinterpret_cast<const bf16x8*>(dout + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
+    }
+    const float lse_l = lse[(size_t)bh * N + qrow] * kLog2e - lw;
+    const float d_l = Drow[(size_t)bh * N + qrow];
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16;
+
+    const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)N * HD * sizeof(bf16));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)N * HD * sizeof(bf16));
+    const int last_row = i * BLK + BLK - 1;
+    const int nkt = CAUSAL ? last_row / kQN + 1 : N / kQN;
+    const int nit = (nkt + 1) / 2;  // iterations: steps 2t (stream 0) and 2t + 1 (stream 1)
+    auto fetch = [&](int t, auto BFC) {
+        constexpr int BF = decltype(BFC)::value;
+        const int kt = 2 * t + stream;
+        if (kt < nkt) {
+            const int soff = kt * kQN * HD * (int)sizeof(bf16);
+            load_tile_to_lds<HD, kQN, NW>(rk, soff, sKV[stream][BF][0], wave, lane);
+            load_tile_to_lds<HD, kQN, NW>(rv, soff, sKV[stream][BF][1], wave, lane);
         }
-        dst[c] = o4;
+    };
+
+    auto step = [&](int t, auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        if (t + 1 < nit) fetch(t + 1, IntC<BUF ^ 1>{});
+        const int kt = 2 * t + stream;
+        const int k0 = kt * kQN;
+        if (kt < nkt && (!CAUSAL || k0 <= qw0 + 31)) {  // a visible key in this wave's step
+            const bf16* sk = sKV[stream][BUF][0];
+            const bf16* sv = sKV[stream][BUF][1];
+            const bool mask = CAUSAL && k0 + kQN - 1 > qw0;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the step
+                f32x16 s, dp;
+                {
+                    bf16x8 ak[KS], av[KS];
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        ak[ks] = frag_at<HD>(sk, 32 * mt, off.frag[ks]);
+                        av[ks] = frag_at<HD>(sv, 32 * mt, off.frag[ks]);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        s = mfma32(ak[ks], qf[ks], ks ? s : zero16);
+                        dp = mfma32(av[ks], of[ks], ks ? dp : zero16);
+                    }
+                    pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
+                }
+                // dS'^T = P' (dP - D) in the accumulator layout (row = key, col = query)
+                bf16x8 da[2];
+                {
+                    float dsv[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float p = fast_exp2(s[r] * scale_log2 - lse_l);
+                        if (mask) {
+                            const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                            if (kk > qrow) p = 0.f;
+                        }
+                        dsv[r] = p * (dp[r] - d_l);
+                    }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        bf16x8 fd;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) fd[e] = to_bf16(dsv[8 * half + e]);
+                        da[half] = fd;
+                    }
+                }
+                // dQ += dS' K over these 32 keys; K^T fragments by transposing reads
+                {
+                    bf16x8 kb[2][DT];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt)
+                            kb[half][dt] = tr_at<HD>(sk, 32 * mt + 16 * half, off.tr[dt]);
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt)
+                            acc[dt] = mfma32(da[half], kb[half][dt], acc[dt]);
+                    pipeline_schedule<4 * DT, 2 * DT, 2, 4>();
+                }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    fetch(0, IntC<0>{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = 0; t < nit; t += 2) {
+        step(t, IntC<0>{});
+        if (t + 1 < nit) step(t + 1, IntC<1>{});
+    }
+
+    // stream 1 hands its partial to stream 0 through LDS (the staging buffers
+    // are free after the last barrier): lane-major, 16 floats per C tile
+    float* red = reinterpret_cast<float*>(&sKV[0][0][0][0]);
+    if (stream == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[((wave * DT + dt) * 16 + r) * 64 + lane] = acc[dt][r];
+    }
+    __syncthreads();
+    if (stream == 0) {
+        // dQ = scale * (partial 0 + partial 1); lane holds column d = 32 dt + l32
+        // of rows 8a + 4hf + bb of this wave's 32 rows
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float x = acc[dt][r] + red[((wave * DT + dt) * 16 + r) * 64 + lane];
+                const int row = 32 * wave + 8 * (r >> 2) + 4 * hf + (r & 3);
+                dq_rows[(size_t)row * HD + 32 * dt + l32] = to_bf16(x * scale);
+            }
     }
 }
 
 // ---------------------------------------------------------------------------
-// float32 path: plain loops, no workspace.
+// float32 path: plain loops.
 // dK/dV: one thread per key row; dQ: one thread per query row.
 // ---------------------------------------------------------------------------
 template <int HD>
@@ -409,23 +717,23 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, float* dq_acc, unsigned phases,
-                      hipStream_t st) {
-    const bool prep = phases & 1u, main = phases & 2u, fin = phases & 4u;
+                      void* dq, void* dk, void* dv, unsigned phases, hipStream_t st) {
+    const bool do_kv = phases & 1u, do_q = phases & 2u;
     if (!pb.bf16) {
-        if (!main) return hipSuccess;
         dim3 gkv((unsigned)((pb.N + 63) / 64), (unsigned)(pb.B * pb.Hkv));
         dim3 gq((unsigned)((pb.N + 63) / 64), (unsigned)(pb.B * pb.Hq));
 #define LF_F32BWD(DD)                                                                          \
     if (pb.d == DD) {                                                                          \
-        hipLaunchKernelGGL(bwd_f32_dkdv_kernel<DD>, gkv, dim3(64), 0, st, (const float*)q,     \
-                           (const float*)k, (const float*)v, lse, (const float*)dout, D,       \
-                           kept_idx, kept_count, block_w, (float*)dk, (float*)dv, pb.Hq,       \
-                           pb.Hkv, pb.N, pb.nqb, pb.block, pb.scale, pb.causal);               \
-        hipLaunchKernelGGL(bwd_f32_dq_kernel<DD>, gq, dim3(64), 0, st, (const float*)q,        \
-                           (const float*)k, (const float*)v, lse, (const float*)dout, D,       \
-                           block_w, (float*)dq, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.block,         \
-                           pb.scale, pb.causal);                                               \
+        if (do_kv)                                                                             \
+            hipLaunchKernelGGL(bwd_f32_dkdv_kernel<DD>, gkv, dim3(64), 0, st, (const float*)q, \
+                               (const float*)k, (const float*)v, lse, (const float*)dout, D,   \
+                               kept_idx, kept_count, block_w, (float*)dk, (float*)dv, pb.Hq,   \
+                               pb.Hkv, pb.N, pb.nqb, pb.block, pb.scale, pb.causal);           \
+        if (do_q)                                                                              \
+            hipLaunchKernelGGL(bwd_f32_dq_kernel<DD>, gq, dim3(64), 0, st, (const float*)q,    \
+                               (const float*)k, (const float*)v, lse, (const float*)dout, D,   \
+                               block_w, (float*)dq, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.block,     \
+                               pb.scale, pb.causal);                                           \
         return hipGetLastError();                                                              \
     }
         LF_F32BWD(64)
@@ -433,24 +741,22 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
 #undef LF_F32BWD
         return hipErrorInvalidValue;
     }
-    const unsigned nblocks = (unsigned)((size_t)pb.B * pb.Hq * pb.nqb);
     const int nkt = (pb.N + kBN - 1) / kBN;
-    const unsigned nwg = (unsigned)(pb.B * pb.Hkv * nkt);
+    const unsigned nwg_kv = (unsigned)(pb.B * pb.Hkv * nkt);
+    const unsigned nwg_q = (unsigned)((size_t)pb.B * pb.Hq * pb.nqb);
     const float sl2 = pb.scale * kLog2e;
 #define LF_BWD(DD, BB, CC)                                                                      \
     if (pb.d == DD && pb.block == BB && (pb.causal != 0) == CC) {                               \
-        if (prep)                                                                               \
-            hipLaunchKernelGGL((dq_zero_kernel<DD, BB>), dim3(nblocks), dim3(256), 0, st,       \
-                               block_w, dq_acc);                                                \
-        if (main)                                                                               \
-            hipLaunchKernelGGL((bwd_bf16_kernel<DD, BB, CC>), dim3(nwg), dim3(256), 0, st,      \
+        if (do_kv)                                                                              \
+            hipLaunchKernelGGL((dkdv_bf16_kernel<DD, BB, CC>), dim3(nwg_kv), dim3(256), 0, st,  \
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
                                (const bf16*)dout, D, kept_idx, kept_count, block_w, (bf16*)dk,  \
-                               (bf16*)dv, dq_acc, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale,  \
-                               sl2);                                                            \
-        if (fin)                                                                                \
-            hipLaunchKernelGGL((dq_convert_kernel<DD, BB>), dim3(nblocks), dim3(256), 0, st,    \
-                               block_w, dq_acc, (bf16*)dq, pb.scale);                           \
+                               (bf16*)dv, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);    \
+        if (do_q)                                                                               \
+            hipLaunchKernelGGL((dq_bf16_kernel<DD, BB, CC>), dim3(nwg_q), dim3(4 * BB), 0, st,  \
+                               (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
+                               (const bf16*)dout, D, block_w, (bf16*)dq, pb.B, pb.Hq, pb.Hkv,   \
+                               pb.N, pb.nqb, pb.scale, sl2);                                    \
         return hipGetLastError();                                                               \
     }
     LF_BWD(64, 64, true)

@@ -68,6 +68,15 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ---- buffer resources ------------------------------------------------------
+// Raw buffer over [base, base + bytes): 32-bit lane offsets plus a uniform
+// scalar offset address it, and accesses past the end read 0 / are dropped.
+constexpr int kBufferConfig = 0x00020000;  // raw 32-bit dword format (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferConfig);
+}
+typedef __attribute__((address_space(3))) void lds_void;
+
 // ---- misc -------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -124,46 +124,33 @@ lf_status lf_block_select(const lf_shape* shape, const void* o, const void* dout
  *                                                           keep*w*dO; rows of
  *                                                           skipped blocks of dq
  *                                                           are exact zeros
- *   workspace, workspace_bytes                         scratch device memory of at
- *                                                      least lf_bwd_workspace_bytes()
- *                                                      bytes, contents undefined on
- *                                                      entry and on return
- * Passing every block kept with weight 1 (lf_block_select with delta = 0)
- * gives the dense backward through the same kernels.
+ * Needs no workspace and is deterministic (no atomics).  Passing every block
+ * kept with weight 1 (lf_block_select with delta = 0) gives the dense backward
+ * through the same kernels.
  */
 lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      void* dq, void* dk, void* dv, void* stream);
 
 /*
- * The three phases of lf_attn_bwd, enqueued separately.  Calling
- * lf_attn_bwd_phases with every bit set is exactly lf_attn_bwd; calling it
- * once per phase, in order, on one stream, with the same arguments and the
- * same workspace, gives the same result.  This lets a caller interleave other
- * work between the phases, or time the tile walk on its own.
- *   LF_BWD_PREPARE   clear the float32 dq accumulator rows of kept blocks
- *   LF_BWD_MAIN      walk the kept blocks: dk, dv and the dq accumulator
- *   LF_BWD_FINALIZE  dq = scale * accumulator (kept rows), 0 (skipped rows)
- * Phases that do not apply to a dtype (the float32 path has one kernel pass,
- * run by LF_BWD_MAIN) enqueue nothing.  An empty or unknown mask is
- * LF_EINVAL.
+ * The two independent halves of lf_attn_bwd, selectable by a bit mask; all
+ * bits together are exactly lf_attn_bwd.  They may run in either order or on
+ * different streams (each reads only the inputs and writes only its own
+ * outputs), which lets a caller overlap them with other work or time them.
+ *   LF_BWD_DKDV  the key-tile walk over kept blocks: writes dk and dv
+ *   LF_BWD_DQ    the query-block walk: writes dq (zeros for skipped blocks)
+ * Unused output pointers of an unselected half may be NULL.  An empty or
+ * unknown mask is LF_EINVAL.
  */
-#define LF_BWD_PREPARE 1u
-#define LF_BWD_MAIN 2u
-#define LF_BWD_FINALIZE 4u
-#define LF_BWD_ALL 7u
+#define LF_BWD_DKDV 1u
+#define LF_BWD_DQ 2u
+#define LF_BWD_ALL 3u
 lf_status lf_attn_bwd_phases(const lf_shape* shape, const void* q, const void* k, const void* v,
                              const float* lse, const void* dout, const float* D,
                              const int32_t* kept_idx, const int32_t* kept_count,
-                             const float* block_w, void* dq, void* dk, void* dv,
-                             void* workspace, size_t workspace_bytes, uint32_t phases,
+                             const float* block_w, void* dq, void* dk, void* dv, uint32_t phases,
                              void* stream);
-
-/* Bytes of device workspace lf_attn_bwd needs for `shape` (0 if the shape is
- * invalid).  Currently the float32 dq accumulator: B*Hq*N*d*4 bytes. */
-size_t lf_bwd_workspace_bytes(const lf_shape* shape);
 
 /* Static, human-readable name of a status code. */
 const char* lf_status_str(lf_status status);
@@ -175,7 +162,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 1
+#define LF_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

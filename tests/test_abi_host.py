@@ -64,9 +64,9 @@ def _sel(lib, shp, delta, ptr=FAKE):
                                ptr, NULL)
 
 
-def _bwd(lib, shp, ws=FAKE, ws_bytes=1 << 40, ptr=FAKE):
+def _bwd(lib, shp, ptr=FAKE):
     return lib.lf_attn_bwd(ctypes.byref(shp), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
-                           ptr, ptr, ws, ws_bytes, NULL)
+                           ptr, ptr, NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -88,7 +88,6 @@ def test_bad_shapes_rejected_by_every_entry_point(kw, status):
     assert lib.lf_last_error() != b""
     assert _sel(lib, shp, 0.1) == status
     assert _bwd(lib, shp) == status
-    assert lib.lf_bwd_workspace_bytes(ctypes.byref(shp)) == 0
 
 
 def test_null_shape_and_null_pointers():
@@ -107,26 +106,13 @@ def test_select_rejects_bad_delta(delta):
     assert b"delta" in lib.lf_last_error()
 
 
-def test_workspace_size_and_check():
-    lib = bd.load()
-    shp = _shape()
-    need = lib.lf_bwd_workspace_bytes(ctypes.byref(shp))
-    assert need == 1 * 4 * 256 * 128 * 4
-    assert _bwd(lib, shp, ws=NULL) == bd.LF_EINVAL
-    assert _bwd(lib, shp, ws_bytes=need - 1) == bd.LF_EINVAL
-    assert b"workspace" in lib.lf_last_error()
-    # the float32 path needs none
-    assert lib.lf_bwd_workspace_bytes(ctypes.byref(_shape(dtype=bd.LF_F32))) == 0
-
-
 def test_empty_problems_are_noops():
     lib = bd.load()
     for kw in (dict(batch=0), dict(seqlen=0)):
         shp = _shape(**kw)
         assert _fwd(lib, shp, ptr=NULL) == bd.LF_OK
         assert _sel(lib, shp, 0.1, ptr=NULL) == bd.LF_OK
-        assert _bwd(lib, shp, ws=NULL, ws_bytes=0, ptr=NULL) == bd.LF_OK
-        assert lib.lf_bwd_workspace_bytes(ctypes.byref(shp)) == 0
+        assert _bwd(lib, shp, ptr=NULL) == bd.LF_OK
     # delta is still checked on an empty problem
     assert _sel(lib, _shape(batch=0), 1.5, ptr=NULL) == bd.LF_EINVAL
 
@@ -141,12 +127,13 @@ def test_bwd_phase_mask_checked():
     lib = bd.load()
     shp = _shape()
 
-    def call(mask):
+    def call(mask, dq=FAKE, dk=FAKE, dv=FAKE):
         return lib.lf_attn_bwd_phases(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                      FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 0, mask, NULL)
+                                      FAKE, FAKE, dq, dk, dv, mask, NULL)
     assert call(0) == bd.LF_EINVAL
-    assert call(8) == bd.LF_EINVAL
+    assert call(4) == bd.LF_EINVAL
     assert b"phase" in lib.lf_last_error()
-    # a valid mask reaches the workspace check
-    assert call(bd.BWD_MAIN) == bd.LF_EINVAL
-    assert b"workspace" in lib.lf_last_error()
+    # each half checks only its own outputs
+    assert call(bd.BWD_DKDV, dk=NULL) == bd.LF_EINVAL
+    assert call(bd.BWD_DQ, dq=NULL) == bd.LF_EINVAL
+    assert b"NULL" in lib.lf_last_error()
