@@ -85,6 +85,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = bd.bwd_workspace(q, k, cfg.block, cfg.causal)
     stream = torch.cuda.current_stream(dev)
 
     def run_steps(delta, seeds):
@@ -100,7 +101,8 @@ def main():
             bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
                             scale=cfg.scale, heads_kv=cfg.Hkv, out=sel)
             ev[2].record(stream)
-            common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv))
+            common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv),
+                          workspace=ws)
             bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DKDV, **common)
             ev[3].record(stream)
             bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DQ, **common)

@@ -12,14 +12,15 @@ import os
 import torch
 
 __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block_select",
-           "select_outputs", "attn_bwd", "EXPORTED_SYMBOLS", "LIB_PATH"]
+           "select_outputs", "attn_bwd", "bwd_workspace_bytes", "bwd_workspace",
+           "EXPORTED_SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
-EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_attn_bwd_phases",
-                    "lf_status_str", "lf_last_error", "lf_abi_version")
+EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_bwd_workspace_size",
+                    "lf_attn_bwd_phases", "lf_status_str", "lf_last_error", "lf_abi_version")
 BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 3
 
 
@@ -55,9 +56,12 @@ def load(path=LIB_PATH):
     lib.lf_attn_fwd.restype = I32
     lib.lf_block_select.argtypes = [S, P, P, D, U64, P, P, P, P, P, P, P]
     lib.lf_block_select.restype = I32
-    lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.lf_attn_bwd.restype = I32
-    lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_uint32, P]
+    lib.lf_bwd_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lf_bwd_workspace_size.restype = I32
+    lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z,
+                                       ctypes.c_uint32, P]
     lib.lf_attn_bwd_phases.restype = I32
     lib.lf_status_str.argtypes = [I32]
     lib.lf_status_str.restype = ctypes.c_char_p
@@ -175,11 +179,28 @@ def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads
     return out
 
 
+def bwd_workspace_bytes(B, Hq, Hkv, N, d, block, causal, dtype):
+    """Device workspace bytes the backward needs for this shape."""
+    lib = load()
+    shp = make_shape(B, Hq, Hkv, N, d, block, causal, d ** -0.5, dtype)
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.lf_bwd_workspace_size(ctypes.byref(shp), ctypes.byref(n)))
+    return n.value
+
+
+def bwd_workspace(q, k, block=128, causal=True):
+    """A workspace tensor (uint8, on q's device) sized for the backward of q, k."""
+    B, Hq, N, d = q.shape
+    n = bwd_workspace_bytes(B, Hq, k.shape[1], N, d, block, causal, q.dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
 def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=None,
-             phases=BWD_ALL):
+             phases=BWD_ALL, workspace=None):
     """Sparse backward over the kept blocks of `sel` (the dict of block_select).
     Returns (dq, dk, dv).  `out` optionally gives preallocated (dq, dk, dv);
-    `phases` selects the dK/dV walk, the dQ walk, or both."""
+    `phases` selects the dK/dV walk, the dQ walk, or both; `workspace`
+    optionally gives a preallocated uint8 device tensor (bwd_workspace)."""
     lib = load()
     shp, _ = _shape_from(q, k, block, causal, scale)
     dev = q.device
@@ -199,9 +220,15 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=No
     _need(dq, "dq", q.shape, q.dtype, dev)
     _need(dk, "dk", k.shape, q.dtype, dev)
     _need(dv, "dv", k.shape, q.dtype, dev)
+    if workspace is None:
+        workspace = bwd_workspace(q, k, block, causal)
+    if (not isinstance(workspace, torch.Tensor) or workspace.device != dev
+            or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on " + str(dev))
+    ws_bytes = workspace.numel() * workspace.element_size()
     args = (ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(sel["D"]),
             _ptr(sel["kept_idx"]), _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq),
-            _ptr(dk), _ptr(dv))
+            _ptr(dk), _ptr(dv), _ptr(workspace), ctypes.c_size_t(ws_bytes))
     if phases == BWD_ALL:
         _check(lib, lib.lf_attn_bwd(*args, _stream(dev)))
     else:

@@ -108,11 +108,21 @@ lf_status lf_block_select(const lf_shape* s, const void* o, const void* dout, do
                                         kept_count, (hipStream_t)stream));
 }
 
+lf_status lf_bwd_workspace_size(const lf_shape* s, size_t* bytes) {
+    lf::Problem pb;
+    bool empty;
+    lf_status st = check_shape(s, pb, empty);
+    if (st != LF_OK) return st;
+    if (!bytes) return fail(LF_EINVAL, "bytes is NULL");
+    *bytes = empty ? 0 : lf::bwd_workspace_bytes(pb);
+    return hip_status(hipSuccess);
+}
+
 lf_status lf_attn_bwd_phases(const lf_shape* s, const void* q, const void* k, const void* v,
                              const float* lse, const void* dout, const float* D,
                              const int32_t* kept_idx, const int32_t* kept_count,
-                             const float* block_w, void* dq, void* dk, void* dv, uint32_t phases,
-                             void* stream) {
+                             const float* block_w, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, uint32_t phases, void* stream) {
     lf::Problem pb;
     bool empty;
     lf_status st = check_shape(s, pb, empty);
@@ -122,16 +132,22 @@ lf_status lf_attn_bwd_phases(const lf_shape* s, const void* q, const void* k, co
     if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w}) ||
         ((phases & LF_BWD_DQ) && !dq) || ((phases & LF_BWD_DKDV) && (!dk || !dv)))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (phases & LF_BWD_DQ) {
+        const size_t need = lf::bwd_workspace_bytes(pb);
+        if (need > 0 && !workspace) return fail(LF_EINVAL, "workspace is NULL");
+        if (workspace_bytes < need) return fail(LF_EINVAL, "workspace too small (see lf_bwd_workspace_size)");
+    }
     return hip_status(lf::launch_bwd(pb, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq,
-                                     dk, dv, phases, (hipStream_t)stream));
+                                     dk, dv, workspace, phases, (hipStream_t)stream));
 }
 
 lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, void* stream) {
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
     return lf_attn_bwd_phases(s, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv,
-                              LF_BWD_ALL, stream);
+                              workspace, workspace_bytes, LF_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -457,172 +457,371 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         }
 }
 
+// ---------------------------------------------------------------------------
+// dQ phase (bf16): plan -> persistent walk -> finalize.
+//
+// The work of a kept block is its key steps (64 keys each) that the causal mask
+// lets it see, so block lengths differ by up to nqb x.  With few kept blocks
+// the longest block would set the run time, so when fewer than 2 * kDqGrid
+// blocks are kept the plan cuts blocks into chunks of about equal length and
+// the chunks' fp32 partials are added in a fixed order by the finalize pass
+// (deterministic).  The persistent kernel takes items from a queue, longest
+// blocks first.
+// ---------------------------------------------------------------------------
+constexpr int kDqGrid = 256;                 // persistent workgroups (one per CU)
+constexpr int kDqMaxSlots = 6 * kDqGrid;     // fp32 partial tiles, see dq_plan_kernel
+constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
+
+struct DqWorkspace {  // carved out of the caller's workspace
+    int* ctrl;        // [0] number of items, [1] queue position
+    int4* items;      // {bh, block, first step | end step << 16, partial slot or -1}
+    int2* blk;        // per (bh, block): {first slot or -1, chunks}
+    float* part;      // [kDqMaxSlots][BLK * HD]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline size_t dq_max_items(size_t nblocks) {
+    return nblocks > (size_t)kDqMaxSlots ? nblocks : (size_t)kDqMaxSlots;
+}
+
+__host__ __device__ inline size_t dq_workspace_bytes(size_t nblocks, int blk, int hd) {
+    return align256(64 * sizeof(int)) + align256(dq_max_items(nblocks) * sizeof(int4)) +
+           align256(nblocks * sizeof(int2)) +
+           (size_t)kDqMaxSlots * blk * hd * sizeof(float);
+}
+
+__host__ __device__ inline DqWorkspace dq_workspace(void* base, size_t nblocks, int blk, int hd) {
+    char* p = static_cast<char*>(base);
+    DqWorkspace w;
+    w.ctrl = reinterpret_cast<int*>(p);
+    p += align256(64 * sizeof(int));
+    w.items = reinterpret_cast<int4*>(p);
+    p += align256(dq_max_items(nblocks) * sizeof(int4));
+    w.blk = reinterpret_cast<int2*>(p);
+    p += align256(nblocks * sizeof(int2));
+    w.part = reinterpret_cast<float*>(p);
+    (void)blk;
+    (void)hd;
+    return w;
+}
+
+// Block-wide exclusive scan of one int per thread (1024 threads); returns the
+// prefix and writes the total to *total.
+__device__ __forceinline__ int block_scan_1024(int x, int* sh, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == 63) sh[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int t = sh[w];
+            sh[w] = run;
+            run += t;
+        }
+        sh[16] = run;
+    }
+    __syncthreads();
+    const int r = sh[wave] + inc - x;
+    *total = sh[16];
+    __syncthreads();
+    return r;
+}
+
+// One workgroup of 1024 threads.  Entries e = 0 .. E-1 run over (block i
+// descending, head bh ascending); an entry is kept when its block weight is
+// non-zero.  Emits the items in that order and the per-block slot table.
+template <int BLK>
+__global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__ block_w, int BHq,
+                                                       int nqb, int N, int causal, DqWorkspace ws) {
+    __shared__ int sh[32];
+    const int E = BHq * nqb;
+    const int tid = threadIdx.x;
+    const int per = (E + 1023) / 1024;
+    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+    auto steps = [&](int i) { return causal ? (i * BLK + BLK - 1) / kQN + 1 : N / kQN; };
+    auto entry = [&](int e, int& bh, int& i) {
+        i = nqb - 1 - e / BHq;
+        bh = e % BHq;
+    };
+    // pass 1: kept blocks K and their total key steps T
+    int kc = 0, ts = 0;
+    for (int e = e0; e < e1; ++e) {
+        int bh, i;
+        entry(e, bh, i);
+        if (block_w[(size_t)bh * nqb + i] != 0.f) {
+            ++kc;
+            ts += steps(i);
+        }
+    }
+    int K, T;
+    block_scan_1024(kc, sh, &K);
+    block_scan_1024(ts, sh, &T);
+    const bool chunking = K < 2 * kDqGrid;
+    const int CL = chunking ? max(kDqMinChunk, (T + 4 * kDqGrid - 1) / (4 * kDqGrid)) : (1 << 30);
+    // pass 2: items and partial slots
+    int ni = 0, nsl = 0;
+    for (int e = e0; e < e1; ++e) {
+        int bh, i;
+        entry(e, bh, i);
+        if (block_w[(size_t)bh * nqb + i] != 0.f) {
+            const int nch = (steps(i) + CL - 1) / CL;
+            ni += nch;
+            nsl += nch > 1 ? nch : 0;
+        }
+    }
+    int n_items, n_slots;
+    int it = block_scan_1024(ni, sh, &n_items);
+    int sl = block_scan_1024(nsl, sh, &n_slots);
+    for (int e = e0; e < e1; ++e) {
+        int bh, i;
+        entry(e, bh, i);
+        int2 info = make_int2(-1, 0);
+        if (block_w[(size_t)bh * nqb + i] != 0.f) {
+            const int L = steps(i);
+            const int nch = (L + CL - 1) / CL;
+            info = make_int2(nch > 1 ? sl : -1, nch);
+            for (int c = 0; c < nch; ++c) {
+                const int s0 = c * CL, s1 = min(L, s0 + CL);
+                ws.items[it++] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
+            }
+            if (nch > 1) sl += nch;
+        }
+        ws.blk[(size_t)bh * nqb + i] = info;
+    }
+    if (tid == 0) {
+        ws.ctrl[0] = n_items;
+        ws.ctrl[1] = 0;
+    }
+}
+
+// Persistent dQ walk.  Each item is one kept block's key steps [s0, s1):
+// two streams of NW waves each (32 query rows per wave) split the steps, even
+// steps to stream 0, odd to stream 1, and add their partials in LDS at the
+// end; the result goes to the dq rows (single-chunk block) or to the item's
+// fp32 partial slot.
 template <int HD, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ Drow,
-    const float* __restrict__ block_w, bf16* __restrict__ dq, int B, int Hq, int Hkv, int N,
-    int nqb, float scale, float scale_log2) {
-    // Two streams of NW waves each (32 query rows per wave) split the key
-    // steps of the block: stream 0 takes the even 64-key steps, stream 1 the
-    // odd ones; their dQ partials are added in LDS at the end (fixed order).
+    const float* __restrict__ block_w, bf16* __restrict__ dq, DqWorkspace ws, int B, int Hq,
+    int Hkv, int N, int nqb, float scale, float scale_log2) {
     constexpr int NW = BLK / 32;
     constexpr int KS = HD / 16;
     constexpr int DT = HD / 32;
     constexpr int TILE = kQN * HD;     // one staged K or V tile (swizzled)
-    static_assert(NW * 64 * DT * 16 * sizeof(float) <= sizeof(bf16) * 2 * 2 * 2 * TILE,
-                  "partial dQ of stream 1 fits in the K/V staging buffers");
+    static_assert(BLK * (HD + 4) * sizeof(float) <= sizeof(bf16) * 2 * 2 * 2 * TILE,
+                  "the fp32 dQ tile fits in the K/V staging buffers");
     __shared__ __attribute__((aligned(16))) bf16 sKV[2][2][2][TILE];   // [stream][buffer][K | V]
+    __shared__ int s_item;
 
-    int b, h, i;
-    map_dq_block(blockIdx.x, B, Hq, Hkv, nqb, CAUSAL, b, h, i);
-    const int g = h / (Hq / Hkv);
-    const int bh = b * Hq + h;
     const int tid = threadIdx.x, lane = tid & 63, wave_all = tid >> 6;
     const int stream = wave_all / NW, wave = wave_all % NW;
     const int l32 = lane & 31, hf = lane >> 5;
-    const size_t qoff = (size_t)bh * N * HD;
-    bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
-
-    const float w = block_w[(size_t)bh * nqb + i];
-    if (w == 0.f) {  // skipped block: its dq rows are exact zeros
-        for (int c = tid; c < BLK * HD / 8; c += 2 * NW * 64)
-            *reinterpret_cast<u32x4*>(dq_rows + 8 * c) = u32x4{};
-        return;
-    }
-    const float lw = __log2f(w);
-    const int qw0 = i * BLK + 32 * wave;  // first row of this wave
-    const int qrow = qw0 + l32;           // query column held by this lane
     const f32x16 zero16 = {};
     const TileOffsets<HD> off(lane);
+    const int n_items = __builtin_amdgcn_readfirstlane(ws.ctrl[0]);
+    const int G = Hq / Hkv;
 
-    // Q^T and dO^T fragments (B operands): column = query, k = head dim
-    bf16x8 qf[KS], of[KS];
+    while (true) {
+        if (tid == 0) s_item = atomicAdd(&ws.ctrl[1], 1);
+        __syncthreads();
+        const int t_item = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        if (t_item >= n_items) break;
+        // the item is wave-uniform: keep it in scalar registers
+        const int4 item = ws.items[t_item];
+        const int bh = __builtin_amdgcn_readfirstlane(item.x);
+        const int i = __builtin_amdgcn_readfirstlane(item.y);
+        const int st0 = __builtin_amdgcn_readfirstlane(item.z & 0xffff);
+        const int st1 = __builtin_amdgcn_readfirstlane(item.z >> 16);
+        const int slot = __builtin_amdgcn_readfirstlane(item.w);
+        const int b = bh / Hq, g = (bh % Hq) / G;
+        const size_t qoff = (size_t)bh * N * HD;
+        const float lw = __log2f(block_w[(size_t)bh * nqb + i]);
+        const int qw0 = i * BLK + 32 * wave;  // first row of this wave
+        const int qrow = qw0 + l32;           // query column held by this lane
+
+        // Q^T and dO^T fragments (B operands): column = query, k = head dim
+        bf16x8 qf[KS], of[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
-        of[ks] = *reinterpret_cast<const bf16x8*>(dout + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
-    }
-    const float lse_l = lse[(size_t)bh * N + qrow] * kLog2e - lw;
-    const float d_l = Drow[(size_t)bh * N + qrow];
-
-    f32x16 acc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16;
-
-    const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)N * HD * sizeof(bf16));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)N * HD * sizeof(bf16));
-    const int last_row = i * BLK + BLK - 1;
-    const int nkt = CAUSAL ? last_row / kQN + 1 : N / kQN;
-    const int nit = (nkt + 1) / 2;  // iterations: steps 2t (stream 0) and 2t + 1 (stream 1)
-    auto fetch = [&](int t, auto BFC) {
-        constexpr int BF = decltype(BFC)::value;
-        const int kt = 2 * t + stream;
-        if (kt < nkt) {
-            const int soff = kt * kQN * HD * (int)sizeof(bf16);
-            load_tile_to_lds<HD, kQN, NW>(rk, soff, sKV[stream][BF][0], wave, lane);
-            load_tile_to_lds<HD, kQN, NW>(rv, soff, sKV[stream][BF][1], wave, lane);
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
+            of[ks] = *reinterpret_cast<const bf16x8*>(dout + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
         }
-    };
+        const float lse_l = lse[(size_t)bh * N + qrow] * kLog2e - lw;
+        const float d_l = Drow[(size_t)bh * N + qrow];
 
-    auto step = [&](int t, auto BUFC) {
-        constexpr int BUF = decltype(BUFC)::value;
-        if (t + 1 < nit) fetch(t + 1, IntC<BUF ^ 1>{});
-        const int kt = 2 * t + stream;
-        const int k0 = kt * kQN;
-        if (kt < nkt && (!CAUSAL || k0 <= qw0 + 31)) {  // a visible key in this wave's step
-            const bf16* sk = sKV[stream][BUF][0];
-            const bf16* sv = sKV[stream][BUF][1];
-            const bool mask = CAUSAL && k0 + kQN - 1 > qw0;
+        f32x16 acc[DT];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the step
-                f32x16 s, dp;
-                {
-                    bf16x8 ak[KS], av[KS];
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16;
+
+        const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)N * HD * sizeof(bf16));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)N * HD * sizeof(bf16));
+        const int nkt = st1 - st0;
+        const int nit = (nkt + 1) / 2;  // iterations: steps 2t (stream 0) and 2t + 1 (stream 1)
+        auto fetch = [&](int t, int BF) {
+            const int kt = 2 * t + stream;
+            if (kt < nkt) {
+                const int soff = (st0 + kt) * kQN * HD * (int)sizeof(bf16);
+                load_tile_to_lds<HD, kQN, NW>(rk, soff, sKV[stream][BF][0], wave, lane);
+                load_tile_to_lds<HD, kQN, NW>(rv, soff, sKV[stream][BF][1], wave, lane);
+            }
+        };
+
+        auto step = [&](int t, int BUF) {
+            if (t + 1 < nit) fetch(t + 1, BUF ^ 1);
+            const int kt = 2 * t + stream;
+            const int k0 = (st0 + kt) * kQN;
+            if (kt < nkt && (!CAUSAL || k0 <= qw0 + 31)) {  // a visible key in this wave's step
+                const bf16* sk = sKV[stream][BUF][0];
+                const bf16* sv = sKV[stream][BUF][1];
+                const bool mask = CAUSAL && k0 + kQN - 1 > qw0;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        ak[ks] = frag_at<HD>(sk, 32 * mt, off.frag[ks]);
-                        av[ks] = frag_at<HD>(sv, 32 * mt, off.frag[ks]);
-                    }
+                for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the step
+                    f32x16 s, dp;
+                    {
+                        bf16x8 ak[KS], av[KS];
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        s = mfma32(ak[ks], qf[ks], ks ? s : zero16);
-                        dp = mfma32(av[ks], of[ks], ks ? dp : zero16);
-                    }
-                    pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
-                }
-                // dS'^T = P' (dP - D) in the accumulator layout (row = key, col = query)
-                bf16x8 da[2];
-                {
-                    float dsv[16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float p = fast_exp2(s[r] * scale_log2 - lse_l);
-                        if (mask) {
-                            const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                            if (kk > qrow) p = 0.f;
+                        for (int ks = 0; ks < KS; ++ks) {
+                            ak[ks] = frag_at<HD>(sk, 32 * mt, off.frag[ks]);
+                            av[ks] = frag_at<HD>(sv, 32 * mt, off.frag[ks]);
                         }
-                        dsv[r] = p * (dp[r] - d_l);
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            s = mfma32(ak[ks], qf[ks], ks ? s : zero16);
+                            dp = mfma32(av[ks], of[ks], ks ? dp : zero16);
+                        }
+                        pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
                     }
+                    // dS'^T = P' (dP - D) in the accumulator layout (row = key, col = query)
+                    bf16x8 da[2];
+                    {
+                        float dsv[16];
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        bf16x8 fd;
+                        for (int r = 0; r < 16; ++r) {
+                            float p = fast_exp2(s[r] * scale_log2 - lse_l);
+                            if (mask) {
+                                const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                                if (kk > qrow) p = 0.f;
+                            }
+                            dsv[r] = p * (dp[r] - d_l);
+                        }
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) fd[e] = to_bf16(dsv[8 * half + e]);
-                        da[half] = fd;
+                        for (int half = 0; half < 2; ++half) {
+                            bf16x8 fd;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) fd[e] = to_bf16(dsv[8 * half + e]);
+                            da[half] = fd;
+                        }
                     }
-                }
-                // dQ += dS' K over these 32 keys; K^T fragments by transposing reads
-                {
-                    bf16x8 kb[2][DT];
+                    // dQ += dS' K over these 32 keys; K^T fragments by transposing reads
+                    {
+                        bf16x8 kb[2][DT];
 #pragma unroll
-                    for (int half = 0; half < 2; ++half)
+                        for (int half = 0; half < 2; ++half)
 #pragma unroll
-                        for (int dt = 0; dt < DT; ++dt)
-                            kb[half][dt] = tr_at<HD>(sk, 32 * mt + 16 * half, off.tr[dt]);
+                            for (int dt = 0; dt < DT; ++dt)
+                                kb[half][dt] = tr_at<HD>(sk, 32 * mt + 16 * half, off.tr[dt]);
 #pragma unroll
-                    for (int half = 0; half < 2; ++half)
+                        for (int half = 0; half < 2; ++half)
 #pragma unroll
-                        for (int dt = 0; dt < DT; ++dt)
-                            acc[dt] = mfma32(da[half], kb[half][dt], acc[dt]);
-                    pipeline_schedule<4 * DT, 2 * DT, 2, 4>();
+                            for (int dt = 0; dt < DT; ++dt)
+                                acc[dt] = mfma32(da[half], kb[half][dt], acc[dt]);
+                        pipeline_schedule<4 * DT, 2 * DT, 2, 4>();
+                    }
                 }
             }
-        }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        };
+
+        fetch(0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-    };
+        for (int t = 0; t < nit; ++t) step(t, t & 1);
 
-    fetch(0, IntC<0>{});
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int t = 0; t < nit; t += 2) {
-        step(t, IntC<0>{});
-        if (t + 1 < nit) step(t + 1, IntC<1>{});
-    }
-
-    // stream 1 hands its partial to stream 0 through LDS (the staging buffers
-    // are free after the last barrier): lane-major, 16 floats per C tile
-    float* red = reinterpret_cast<float*>(&sKV[0][0][0][0]);
-    if (stream == 1) {
+        // Both streams' partials meet in a row-major fp32 tile in LDS (the
+        // staging buffers are free after the last barrier; rows padded by 4
+        // floats so the two half-waves hit different banks): stream 1 stores,
+        // stream 0 adds, then every thread writes 16-byte row pieces.
+        float* red = reinterpret_cast<float*>(&sKV[0][0][0][0]);
+        constexpr int RS = HD + 4;  // row stride of the tile, floats
+        float* rw = red + (32 * wave + 4 * hf) * RS + l32;  // row 4hf, column l32 of this wave
+        if (stream == 1) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[((wave * DT + dt) * 16 + r) * 64 + lane] = acc[dt][r];
-    }
-    __syncthreads();
-    if (stream == 0) {
-        // dQ = scale * (partial 0 + partial 1); lane holds column d = 32 dt + l32
-        // of rows 8a + 4hf + bb of this wave's 32 rows
+                for (int r = 0; r < 16; ++r) rw[(8 * (r >> 2) + (r & 3)) * RS + 32 * dt] = acc[dt][r];
+        }
+        __syncthreads();
+        if (stream == 0) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = acc[dt][r] + red[((wave * DT + dt) * 16 + r) * 64 + lane];
-                const int row = 32 * wave + 8 * (r >> 2) + 4 * hf + (r & 3);
-                dq_rows[(size_t)row * HD + 32 * dt + l32] = to_bf16(x * scale);
+                for (int r = 0; r < 16; ++r) rw[(8 * (r >> 2) + (r & 3)) * RS + 32 * dt] += acc[dt][r];
+        }
+        __syncthreads();
+        // scale * tile -> dq rows (bf16) or the item's partial slot (fp32)
+        constexpr int NV = BLK * HD / 8;  // 8-float pieces
+        if (slot < 0) {
+            bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
+            for (int c = tid; c < NV; c += 2 * NW * 64) {
+                const int row = c / (HD / 8), col = 8 * (c % (HD / 8));
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(red + row * RS + col);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(red + row * RS + col + 4);
+                bf16x8 o;
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    o[z] = to_bf16(x0[z] * scale);
+                    o[4 + z] = to_bf16(x1[z] * scale);
+                }
+                *reinterpret_cast<bf16x8*>(dq_rows + (size_t)row * HD + col) = o;
             }
+        } else {
+            float* part = ws.part + (size_t)slot * BLK * HD;
+            for (int c = tid; c < NV; c += 2 * NW * 64) {
+                const int row = c / (HD / 8), col = 8 * (c % (HD / 8));
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(red + row * RS + col);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(red + row * RS + col + 4);
+                *reinterpret_cast<f32x4*>(part + (size_t)row * HD + col) = x0 * scale;
+                *reinterpret_cast<f32x4*>(part + (size_t)row * HD + col + 4) = x1 * scale;
+            }
+        }
+        __syncthreads();  // the staging buffers are reused by the next item
+    }
+}
+
+// dq rows of every block: zeros for skipped blocks, the in-order sum of the
+// partial slots for chunked blocks; single-chunk blocks were written already.
+template <int HD, int BLK>
+__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ block_w,
+                                                          DqWorkspace ws, bf16* __restrict__ dq) {
+    const size_t e = blockIdx.x;  // (bh, block) in memory order
+    bf16x4* out = reinterpret_cast<bf16x4*>(dq + e * BLK * HD);
+    if (block_w[e] == 0.f) {
+        for (int c = threadIdx.x; c < BLK * HD / 4; c += 256) out[c] = bf16x4{};
+        return;
+    }
+    const int2 info = ws.blk[e];
+    if (info.x < 0) return;
+    for (int c = threadIdx.x; c < BLK * HD / 4; c += 256) {
+        f32x4 s = reinterpret_cast<const f32x4*>(ws.part + (size_t)info.x * BLK * HD)[c];
+        for (int j = 1; j < info.y; ++j) {
+            const f32x4 x = reinterpret_cast<const f32x4*>(ws.part + (size_t)(info.x + j) * BLK * HD)[c];
+            s += x;
+        }
+        bf16x4 o;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) o[z] = to_bf16(s[z]);
+        out[c] = o;
     }
 }
 
@@ -714,10 +913,16 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
+size_t bwd_workspace_bytes(const Problem& pb) {
+    if (!pb.bf16) return 0;
+    return dq_workspace_bytes((size_t)pb.B * pb.Hq * pb.nqb, pb.block, pb.d);
+}
+
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, unsigned phases, hipStream_t st) {
+                      void* dq, void* dk, void* dv, void* workspace, unsigned phases,
+                      hipStream_t st) {
     const bool do_kv = phases & 1u, do_q = phases & 2u;
     if (!pb.bf16) {
         dim3 gkv((unsigned)((pb.N + 63) / 64), (unsigned)(pb.B * pb.Hkv));
@@ -743,8 +948,9 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     }
     const int nkt = (pb.N + kBN - 1) / kBN;
     const unsigned nwg_kv = (unsigned)(pb.B * pb.Hkv * nkt);
-    const unsigned nwg_q = (unsigned)((size_t)pb.B * pb.Hq * pb.nqb);
+    const size_t nblocks = (size_t)pb.B * pb.Hq * pb.nqb;
     const float sl2 = pb.scale * kLog2e;
+    const DqWorkspace ws = dq_workspace(workspace, nblocks, pb.block, pb.d);
 #define LF_BWD(DD, BB, CC)                                                                      \
     if (pb.d == DD && pb.block == BB && (pb.causal != 0) == CC) {                               \
         if (do_kv)                                                                              \
@@ -752,11 +958,16 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
                                (const bf16*)dout, D, kept_idx, kept_count, block_w, (bf16*)dk,  \
                                (bf16*)dv, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);    \
-        if (do_q)                                                                               \
-            hipLaunchKernelGGL((dq_bf16_kernel<DD, BB, CC>), dim3(nwg_q), dim3(4 * BB), 0, st,  \
+        if (do_q) {                                                                             \
+            hipLaunchKernelGGL((dq_plan_kernel<BB>), dim3(1), dim3(1024), 0, st, block_w,       \
+                               pb.B * pb.Hq, pb.nqb, pb.N, pb.causal, ws);                      \
+            hipLaunchKernelGGL((dq_bf16_kernel<DD, BB, CC>), dim3(kDqGrid), dim3(4 * BB), 0, st, \
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
-                               (const bf16*)dout, D, block_w, (bf16*)dq, pb.B, pb.Hq, pb.Hkv,   \
-                               pb.N, pb.nqb, pb.scale, sl2);                                    \
+                               (const bf16*)dout, D, block_w, (bf16*)dq, ws, pb.B, pb.Hq,       \
+                               pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);                            \
+            hipLaunchKernelGGL((dq_finalize_kernel<DD, BB>), dim3((unsigned)nblocks), dim3(256), \
+                               0, st, block_w, ws, (bf16*)dq);                                  \
+        }                                                                                       \
         return hipGetLastError();                                                               \
     }
     LF_BWD(64, 64, true)

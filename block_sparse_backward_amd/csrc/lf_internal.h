@@ -23,7 +23,11 @@ hipError_t launch_select(const Problem& pb, const void* o, const void* dout, dou
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, unsigned phases, hipStream_t st);
+                      void* dq, void* dk, void* dv, void* workspace, unsigned phases,
+                      hipStream_t st);
+
+// Device workspace bytes of launch_bwd for a validated problem (0 for fp32).
+size_t bwd_workspace_bytes(const Problem& pb);
 
 // Workgroup -> work-item maps that keep every workgroup of one key/value head
 // group on one XCD (workgroups are dispatched round-robin over the 8 XCDs, each

@@ -35,9 +35,10 @@
  *     Query head h reads key/value head h / (Hq / Hkv).
  *   - All tensor pointers are DEVICE pointers owned by the caller; outputs are
  *     fully overwritten (never accumulated into).  The library allocates
- *     nothing and keeps no state between calls; work is enqueued on `stream`
- *     (a hipStream_t; NULL = the default stream) and the call returns without
- *     waiting for it.
+ *     nothing and keeps no state between calls; scratch memory, where an entry
+ *     point needs it, is a caller-owned workspace argument.  Work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *     returns without waiting for it.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failed check returns LF_EINVAL (malformed) or LF_EUNSUPPORTED (valid
  *     but outside what the kernels implement) and launches nothing.  A failed
@@ -124,14 +125,30 @@ lf_status lf_block_select(const lf_shape* shape, const void* o, const void* dout
  *                                                           keep*w*dO; rows of
  *                                                           skipped blocks of dq
  *                                                           are exact zeros
- * Needs no workspace and is deterministic (no atomics).  Passing every block
- * kept with weight 1 (lf_block_select with delta = 0) gives the dense backward
- * through the same kernels.
+ *   workspace, workspace_bytes                         scratch: device memory of at
+ *                                                           least lf_bwd_workspace_size
+ *                                                           bytes, owned by the caller
+ * The result is deterministic: bit-identical on every call with the same
+ * inputs (no floating-point atomics; partial sums are added in a fixed
+ * order).  The workspace needs no initialisation and holds nothing useful
+ * afterwards; calls that may overlap (other streams) need workspaces of their
+ * own.  Too small a workspace, or NULL with a nonzero size requirement, is
+ * LF_EINVAL.  Passing every block kept with weight 1 (lf_block_select with
+ * delta = 0) gives the dense backward through the same kernels.
  */
 lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,
                       const int32_t* kept_idx, const int32_t* kept_count, const float* block_w,
-                      void* dq, void* dk, void* dv, void* stream);
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Workspace bytes that lf_attn_bwd and lf_attn_bwd_phases need for `shape`
+ * (written to *bytes).  It depends on the shape only: at most
+ * 6144 * block * head_dim + 24 * B * Hq * nqb + 26 KiB, about 100 MB for
+ * block = head_dim = 128, and 0 for LF_F32.  Shape errors as in lf_attn_bwd.
+ */
+lf_status lf_bwd_workspace_size(const lf_shape* shape, size_t* bytes);
 
 /*
  * The two independent halves of lf_attn_bwd, selectable by a bit mask; all
@@ -139,9 +156,11 @@ lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const
  * different streams (each reads only the inputs and writes only its own
  * outputs), which lets a caller overlap them with other work or time them.
  *   LF_BWD_DKDV  the key-tile walk over kept blocks: writes dk and dv
- *   LF_BWD_DQ    the query-block walk: writes dq (zeros for skipped blocks)
- * Unused output pointers of an unselected half may be NULL.  An empty or
- * unknown mask is LF_EINVAL.
+ *   LF_BWD_DQ    the query-block walk: writes dq (zeros for skipped blocks);
+ *                the only half that uses the workspace
+ * Unused output pointers of an unselected half, and the workspace when
+ * LF_BWD_DQ is not selected, may be NULL.  An empty or unknown mask is
+ * LF_EINVAL.
  */
 #define LF_BWD_DKDV 1u
 #define LF_BWD_DQ 2u
@@ -149,8 +168,8 @@ lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const
 lf_status lf_attn_bwd_phases(const lf_shape* shape, const void* q, const void* k, const void* v,
                              const float* lse, const void* dout, const float* D,
                              const int32_t* kept_idx, const int32_t* kept_count,
-                             const float* block_w, void* dq, void* dk, void* dv, uint32_t phases,
-                             void* stream);
+                             const float* block_w, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, uint32_t phases, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* lf_status_str(lf_status status);
@@ -162,7 +181,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 2
+#define LF_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

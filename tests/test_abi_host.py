@@ -64,9 +64,18 @@ def _sel(lib, shp, delta, ptr=FAKE):
                                ptr, NULL)
 
 
-def _bwd(lib, shp, ptr=FAKE):
+BIG = 1 << 40  # workspace bytes larger than any requirement
+
+
+def _bwd(lib, shp, ptr=FAKE, ws=FAKE, ws_bytes=BIG):
     return lib.lf_attn_bwd(ctypes.byref(shp), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
-                           ptr, ptr, NULL)
+                           ptr, ptr, ws, ws_bytes, NULL)
+
+
+def _ws_size(lib, shp):
+    n = ctypes.c_size_t(12345)
+    st = lib.lf_bwd_workspace_size(ctypes.byref(shp), ctypes.byref(n))
+    return st, n.value
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -88,6 +97,7 @@ def test_bad_shapes_rejected_by_every_entry_point(kw, status):
     assert lib.lf_last_error() != b""
     assert _sel(lib, shp, 0.1) == status
     assert _bwd(lib, shp) == status
+    assert _ws_size(lib, shp)[0] == status
 
 
 def test_null_shape_and_null_pointers():
@@ -129,7 +139,7 @@ def test_bwd_phase_mask_checked():
 
     def call(mask, dq=FAKE, dk=FAKE, dv=FAKE):
         return lib.lf_attn_bwd_phases(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                      FAKE, FAKE, dq, dk, dv, mask, NULL)
+                                      FAKE, FAKE, dq, dk, dv, FAKE, BIG, mask, NULL)
     assert call(0) == bd.LF_EINVAL
     assert call(4) == bd.LF_EINVAL
     assert b"phase" in lib.lf_last_error()
@@ -137,3 +147,25 @@ def test_bwd_phase_mask_checked():
     assert call(bd.BWD_DKDV, dk=NULL) == bd.LF_EINVAL
     assert call(bd.BWD_DQ, dq=NULL) == bd.LF_EINVAL
     assert b"NULL" in lib.lf_last_error()
+
+
+def test_workspace_size_and_checks():
+    lib = bd.load()
+    # bf16: fp32 partial tiles of 1536 blocks plus the item and block tables
+    shp = _shape(batch=2, heads_q=4, heads_kv=2, seqlen=1024, head_dim=128, block=128)
+    st, n = _ws_size(lib, shp)
+    nblocks = 2 * 4 * 1024 // 128
+    assert st == bd.LF_OK
+    assert 1536 * 128 * 128 * 4 <= n <= 1536 * 128 * 128 * 4 + 24 * nblocks + 26 * 1024
+    # grows with the number of blocks once they exceed the partial slots
+    st2, n2 = _ws_size(lib, _shape(batch=64, heads_q=32, heads_kv=8, seqlen=8192,
+                                   head_dim=128, block=128))
+    assert st2 == bd.LF_OK and n2 > n
+    assert _ws_size(lib, _shape(dtype=bd.LF_F32)) == (bd.LF_OK, 0)
+    assert _ws_size(lib, _shape(batch=0)) == (bd.LF_OK, 0)
+    assert lib.lf_bwd_workspace_size(ctypes.byref(shp), None) == bd.LF_EINVAL
+    # the backward refuses a missing or short workspace before launching anything
+    assert _bwd(lib, shp, ws=NULL) == bd.LF_EINVAL
+    assert b"workspace" in lib.lf_last_error()
+    assert _bwd(lib, shp, ws_bytes=n - 1) == bd.LF_EINVAL
+    assert b"workspace" in lib.lf_last_error()
