@@ -115,6 +115,34 @@ __device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t rs, int 
     }
 }
 
+// The same swizzled tile, fetched in two halves through registers: issue()
+// starts this lane's 16-byte loads (coalesced rows), commit() stores them to
+// their swizzled LDS places.  Unlike loads to LDS, a fetch in flight does not
+// hold back the LDS reads of the tile being computed (the compiler cannot tell
+// a load-to-LDS target apart from the tile being read and waits for it).
+template <int HD, int ROWS, int NWAVES>
+struct TileFetch {
+    static constexpr int CPR = HD / 8;
+    static constexpr int NPER = ROWS * CPR / (64 * NWAVES);
+    static_assert(ROWS * CPR % (64 * NWAVES) == 0, "whole rounds");
+    u32x4 r[NPER];
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int soff, int wave, int lane) {
+#pragma unroll
+        for (int m = 0; m < NPER; ++m) {
+            const int S = 64 * (wave + NWAVES * m) + lane;
+            r[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, (S / CPR * HD + S % CPR * 8) * 2, soff, 0);
+        }
+    }
+    __device__ __forceinline__ void commit(bf16* lds, int wave, int lane) const {
+#pragma unroll
+        for (int m = 0; m < NPER; ++m) {
+            const int S = 64 * (wave + NWAVES * m) + lane;
+            const int row = S / CPR, c = (S % CPR) ^ swz<HD>(row);
+            *reinterpret_cast<u32x4*>(lds + row * HD + c * 8) = r[m];
+        }
+    }
+};
+
 // Per-lane byte offsets into a swizzled tile, fixed for the kernel's life:
 //   frag[ks]    32x32x16 operand fragment of row (R + l32), head-dim chunk
 //               2 ks + hf, for any R that is a multiple of 16;
@@ -317,25 +345,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     // one-register path (they are transformed on the way).
     float pld = 0.f;
     const uint32_t head_bytes = (uint32_t)N * HD * sizeof(bf16);
+    TileFetch<HD, kBM, 4> fq, fo;
     auto fetch = [&](int bh, int qs0, float lw, int BF) {
+        (void)lw;
+        (void)BF;
         const size_t hoff = (size_t)bh * N * HD;
         const int soff = qs0 * HD * (int)sizeof(bf16);
-        load_tile_to_lds<HD, kBM, 4>(make_rsrc(q + hoff, head_bytes), soff, sQD[BF][0], wave, lane);
-        load_tile_to_lds<HD, kBM, 4>(make_rsrc(dout + hoff, head_bytes), soff, sQD[BF][1], wave,
-                                     lane);
-        if (tid < kBM) pld = lse[(size_t)bh * N + qs0 + tid] * kLog2e - lw;
+        fq.issue(make_rsrc(q + hoff, head_bytes), soff, wave, lane);
+        fo.issue(make_rsrc(dout + hoff, head_bytes), soff, wave, lane);
+        // raw values only: any arithmetic on them here would make the wave wait
+        // for this load, and with it for the tile loads issued just before
+        if (tid < kBM) pld = lse[(size_t)bh * N + qs0 + tid];
         else if (tid < 2 * kBM) pld = Drow[(size_t)bh * N + qs0 + tid - kBM];
     };
-    auto stage = [&](int BF) {
-        if (tid < 2 * kBM) sLD[BF][tid / kBM][tid % kBM] = pld;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and D
+    auto stage = [&](int BF, float lw) {
+        fq.commit(sQD[BF][0], wave, lane);
+        fo.commit(sQD[BF][1], wave, lane);
+        if (tid < kBM) sLD[BF][0][tid] = pld * kLog2e - lw;
+        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld;
     };
 
     if (W.first()) {
         int cur_bh = W.bh, cur_q0 = W.q0();
         float cur_lw = W.lw;
         fetch(cur_bh, cur_q0, cur_lw, 0);
-        stage(0);
+        stage(0, cur_lw);
         __syncthreads();
 
         // One sub-tile, one 32-row query tile at a time: S and dP, then P' and
@@ -433,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             fetch(nx_bh, nx_q0, nx_lw, buf ^ 1);
             const bool mask = (CAUSAL && k0 + kBN - 1 > cur_q0) || (k0 + kBN > N);
             body(buf, mask);
-            stage(buf ^ 1);
+            stage(buf ^ 1, nx_lw);
             __syncthreads();
             if (!more) break;
             buf ^= 1;
