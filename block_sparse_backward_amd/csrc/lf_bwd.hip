@@ -133,13 +133,14 @@ struct TileFetch {
             r[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, (S / CPR * HD + S % CPR * 8) * 2, soff, 0);
         }
     }
+    __device__ __forceinline__ void commit_one(bf16* lds, int wave, int lane, int m) const {
+        const int S = 64 * (wave + NWAVES * m) + lane;
+        const int row = S / CPR, c = (S % CPR) ^ swz<HD>(row);
+        *reinterpret_cast<u32x4*>(lds + row * HD + c * 8) = r[m];
+    }
     __device__ __forceinline__ void commit(bf16* lds, int wave, int lane) const {
 #pragma unroll
-        for (int m = 0; m < NPER; ++m) {
-            const int S = 64 * (wave + NWAVES * m) + lane;
-            const int row = S / CPR, c = (S % CPR) ^ swz<HD>(row);
-            *reinterpret_cast<u32x4*>(lds + row * HD + c * 8) = r[m];
-        }
+        for (int m = 0; m < NPER; ++m) commit_one(lds, wave, lane, m);
     }
 };
 
@@ -194,6 +195,24 @@ __device__ __forceinline__ void pipeline_schedule() {
     for (int i = 0; i < steps; ++i) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kDsRead, PER, 0);
+    }
+    if (rest % PER) __builtin_amdgcn_sched_group_barrier(kDsRead, rest % PER, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, NM - steps, 0);
+}
+
+// As pipeline_schedule, with NV buffer loads of other work issued one per MFMA
+// from the first MFMA on.
+template <int NR, int NM, int PER, int AHEAD, int NV>
+__device__ __forceinline__ void pipeline_schedule_vmem() {
+    constexpr int kDsRead = 0x100, kMfma = 0x008, kVmemRead = 0x020;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD, 0);
+    constexpr int rest = NR - AHEAD;
+    constexpr int steps = rest / PER;
+#pragma unroll
+    for (int i = 0; i < steps; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, PER, 0);
+        if (i < NV) __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
     }
     if (rest % PER) __builtin_amdgcn_sched_group_barrier(kDsRead, rest % PER, 0);
     __builtin_amdgcn_sched_group_barrier(kMfma, NM - steps, 0);
@@ -286,6 +305,16 @@ struct IntC {
     static constexpr int value = V;
 };
 
+// acc += a b with the accumulator held in AGPRs for the whole walk (the
+// register allocator otherwise moves accumulator tiles through VGPRs around
+// the score products).  The A operand may have just been written by a VALU
+// op, which needs two wait states before an MFMA reads it; dependent
+// accumulations need none.  The caller waits out the result latency before
+// reading the accumulator with anything but this.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 template <int HD, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -297,9 +326,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     constexpr int DT = HD / 32;        // 32-wide head-dim tiles
     constexpr int TILE = kBM * HD;     // one staged Q or dO tile (swizzled)
 
-    // double-buffered staging: [buffer][Q | dO], LSE' | D per buffer
-    __shared__ __attribute__((aligned(16))) bf16 sQD[2][2][TILE];
-    __shared__ __attribute__((aligned(16))) float sLD[2][2][kBM];
+    // staging, three buffers: the sub-tile being computed, the previous one
+    // (its last dV/dK products run alongside this one's first softmax) and the
+    // next one; [buffer][Q | dO], LSE' | D per buffer
+    __shared__ __attribute__((aligned(16))) bf16 sQD[3][2][TILE];
+    __shared__ __attribute__((aligned(16))) float sLD[3][2][kBM];
 
     int b, g, j;
     map_bwd_block(blockIdx.x, B, Hkv, b, g, j);
@@ -354,129 +385,186 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         fq.issue(make_rsrc(q + hoff, head_bytes), soff, wave, lane);
         fo.issue(make_rsrc(dout + hoff, head_bytes), soff, wave, lane);
         // raw values only: any arithmetic on them here would make the wave wait
-        // for this load, and with it for the tile loads issued just before
-        if (tid < kBM) pld = lse[(size_t)bh * N + qs0 + tid];
-        else if (tid < 2 * kBM) pld = Drow[(size_t)bh * N + qs0 + tid - kBM];
+        // for this load, and with it for the tile loads issued just before.
+        // Threads 0..63 load LSE, the others D (two waves load it twice): no
+        // branch, so the loads can share a scheduling region with MFMAs.
+        pld = (tid < kBM ? lse : Drow)[(size_t)bh * N + qs0 + (tid & (kBM - 1))];
     };
     // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and D
+    auto stage_rows = [&](int BF, float lw) {
+        if (tid < kBM) sLD[BF][0][tid] = pld * kLog2e - lw;
+        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld;
+    };
     auto stage = [&](int BF, float lw) {
         fq.commit(sQD[BF][0], wave, lane);
         fo.commit(sQD[BF][1], wave, lane);
-        if (tid < kBM) sLD[BF][0][tid] = pld * kLog2e - lw;
-        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld;
+        stage_rows(BF, lw);
+    };
+    constexpr int NPIECE = decltype(fq)::NPER;
+
+    // S = Q K_w^T and dP = dO V_w^T for one 32-row query tile (A: LDS rows,
+    // B: the K/V fragments in registers)
+    auto sdp = [&](const bf16* sq, const bf16* sdo, int qt, f32x16& s, f32x16& dp, auto&& pre) {
+        pre();  // other work issued alongside (the next sub-tile's loads)
+        bf16x8 aq[KS], ao[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            aq[ks] = frag_at<HD>(sq, 32 * qt, off.frag[ks]);
+            ao[ks] = frag_at<HD>(sdo, 32 * qt, off.frag[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = mfma32(aq[ks], kf[ks], ks ? s : zero16);
+            dp = mfma32(ao[ks], vf[ks], ks ? dp : zero16);
+        }
+        pipeline_schedule_vmem<2 * KS, 2 * KS, 1, 6, 2 * NPIECE + 1>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One softmax and one dV/dK step, interleaved in 4*DT chunks: chunk m
+    // issues the transposing reads of MFMA m + kAhead, runs dV/dK MFMA m of
+    // query tile `dqt` of the tiles (tq, tdo) with the P', dS' operands
+    // (ipa, ida), and turns score elements of query tile `qt` into P' and dS'
+    // (opa, oda).  With `SM` false only the dV/dK part runs.
+    //   dV_w += P'^T dO,  dK_w += dS'^T Q  (A: P'/dS' in the score layout,
+    //   B: transposing LDS reads of the row-major tiles)
+    //   P' = exp2(s scale log2 e - LSE'), zero where the mask hides the pair,
+    //   dS' = P' (dP - D), element (row ql, this lane's key) kept iff ql >= thr
+    constexpr int kAhead = 3;
+    constexpr int NMF = 4 * DT;  // dV/dK MFMAs per 32-row tile
+    auto sm_dvdk = [&](auto SMC, const f32x16& s, const f32x16& dp, const float* sl,
+                       const float* sd, int qt, int thr, bf16x8 (&opa)[2], bf16x8 (&oda)[2],
+                       const bf16* tq, const bf16* tdo, int dqt, const bf16x8 (&ipa)[2],
+                       const bf16x8 (&ida)[2], auto&& extra) {
+        constexpr bool SM = decltype(SMC)::value != 0;
+        constexpr int EPC = (16 + NMF - 1) / NMF;  // softmax elements per chunk
+        auto bfrag = [&](int m) {  // B operand of MFMA m: (half, dt, dV | dK)
+            return tr_at<HD>((m & 1) ? tq : tdo, 32 * dqt + 16 * (m / (2 * DT)),
+                             off.tr[(m >> 1) % DT]);
+        };
+        bf16x8 bf[NMF];
+        f32x4 L4[4], D4[4];
+        float pv[16], dsv[16];
+        if constexpr (SM) {
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+                L4[a2] = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a2 + 4 * hf);
+                D4[a2] = *reinterpret_cast<const f32x4*>(sd + 32 * qt + 8 * a2 + 4 * hf);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kAhead; ++m) bf[m] = bfrag(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            if (m + kAhead < NMF) bf[m + kAhead] = bfrag(m + kAhead);
+            if (SM && (m * EPC) % 4 == 0 && (m * EPC) / 4 + 2 < 4) {
+                const int a2 = (m * EPC) / 4 + 2;
+                L4[a2] = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a2 + 4 * hf);
+                D4[a2] = *reinterpret_cast<const f32x4*>(sd + 32 * qt + 8 * a2 + 4 * hf);
+            }
+            const int half = m / (2 * DT), dt = (m >> 1) % DT;
+            if (m & 1) mfma32_agpr(acc_dk[dt], ida[half], bf[m]);
+            else mfma32_agpr(acc_dv[dt], ipa[half], bf[m]);
+            if constexpr (SM) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    const int r = m * EPC + e;
+                    if (r < 16) {
+                        const int a2 = r >> 2, bb = r & 3;
+                        float p = fast_exp2(s[r] * scale_log2 - L4[a2][bb]);
+                        if (32 * qt + 8 * a2 + bb < thr) p = 0.f;
+                        pv[r] = p;
+                        dsv[r] = p * (dp[r] - D4[a2][bb]);
+                        if (r & 1) {
+                            opa[r >> 3][(r & 7) - 1] = to_bf16(pv[r - 1]);
+                            opa[r >> 3][r & 7] = to_bf16(pv[r]);
+                            oda[r >> 3][(r & 7) - 1] = to_bf16(dsv[r - 1]);
+                            oda[r >> 3][r & 7] = to_bf16(dsv[r]);
+                        }
+                    }
+                }
+            }
+            extra(m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SM) {
+            // keep P', dS' computed here, interleaved with the MFMAs, even when
+            // their only use is in the next iteration (the compiler would
+            // otherwise sink the softmax past the loop's barrier)
+            asm volatile("" : "+v"(opa[0]), "+v"(opa[1]), "+v"(oda[0]), "+v"(oda[1]));
+        }
     };
 
     if (W.first()) {
         int cur_bh = W.bh, cur_q0 = W.q0();
         float cur_lw = W.lw;
         fetch(cur_bh, cur_q0, cur_lw, 0);
+        {   // the "previous" tiles of the first sub-tile hold zeros, so the
+            // pipeline's first dV/dK step (with zero P', dS') adds exact zeros
+            u32x4* z = reinterpret_cast<u32x4*>(&sQD[2][0][0]);
+            for (int c = tid; c < 2 * TILE / 8; c += 256) z[c] = u32x4{};
+        }
         stage(0, cur_lw);
         __syncthreads();
 
-        // One sub-tile, one 32-row query tile at a time: S and dP, then P' and
-        // dS' in the accumulator layout, then the dV/dK k-steps over those rows.
-        auto body = [&](int BUF, bool mask) {
-            // element (query row ql, this lane's key) is kept iff ql >= thr:
-            // causal needs key <= cur_q0 + ql; keys past N are never kept
-            const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
-            const bf16* sq = sQD[BUF][0];
-            const bf16* sdo = sQD[BUF][1];
-            const float* sl = sLD[BUF][0];
-            const float* sd = sLD[BUF][1];
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                f32x16 s, dp;
-                {
-                    bf16x8 aq[KS], ao[KS];
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        aq[ks] = frag_at<HD>(sq, 32 * qt, off.frag[ks]);
-                        ao[ks] = frag_at<HD>(sdo, 32 * qt, off.frag[ks]);
-                    }
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        s = mfma32(aq[ks], kf[ks], ks ? s : zero16);
-                        dp = mfma32(ao[ks], vf[ks], ks ? dp : zero16);
-                    }
-                    pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                bf16x8 pa[2], da[2];
-                {
-                    float pv[16], dsv[16];
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a + 4 * hf);
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb)
-                            pv[4 * a + bb] = fast_exp2(s[4 * a + bb] * scale_log2 - L4[bb]);
-                    }
-                    if (mask) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (32 * qt + 8 * (r >> 2) + (r & 3) < thr) pv[r] = 0.f;
-                    }
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const f32x4 D4 = *reinterpret_cast<const f32x4*>(sd + 32 * qt + 8 * a + 4 * hf);
-#pragma unroll
-                        for (int bb = 0; bb < 4; ++bb)
-                            dsv[4 * a + bb] = pv[4 * a + bb] * (dp[4 * a + bb] - D4[bb]);
-                    }
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        bf16x8 fp, fd;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            fp[e] = to_bf16(pv[8 * half + e]);
-                            fd[e] = to_bf16(dsv[8 * half + e]);
-                        }
-                        pa[half] = fp;
-                        da[half] = fd;
-                    }
-                }
-                // dV_w += P'^T dO, dK_w += dS'^T Q over these 32 query rows
-                {
-                    bf16x8 bo[2][DT], bq[2][DT];
-#pragma unroll
-                    for (int half = 0; half < 2; ++half)
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            bo[half][dt] = tr_at<HD>(sdo, 32 * qt + 16 * half, off.tr[dt]);
-                            bq[half][dt] = tr_at<HD>(sq, 32 * qt + 16 * half, off.tr[dt]);
-                        }
-#pragma unroll
-                    for (int half = 0; half < 2; ++half)
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            acc_dv[dt] = mfma32(pa[half], bo[half][dt], acc_dv[dt]);
-                            acc_dk[dt] = mfma32(da[half], bq[half][dt], acc_dk[dt]);
-                        }
-                    pipeline_schedule<8 * DT, 4 * DT, 2, 8>();
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-
-        int buf = 0;
+        // Pipeline over sub-tiles t (buffer t % 3), two 32-row tiles each:
+        //   S,dP(t,0) | softmax(t,0) + dV,dK(t-1,1) | S,dP(t,1) | softmax(t,1) + dV,dK(t,0)
+        // and dV,dK(last,1) after the walk.
+        const IntC<1> with_softmax;
+        const IntC<0> no_softmax;
+        bf16x8 ppa[2] = {}, pda[2] = {};  // P', dS' of the previous sub-tile's second tile
+        int buf = 0, pbuf = 2;
         while (true) {
-            // prefetch the next sub-tile (or reload this one when none is left)
             const bool more = W.next();
+            const int fbuf = buf == 2 ? 0 : buf + 1;  // the buffer of t-2, free since the barrier
+            // the next sub-tile (this one again after the last: a harmless
+            // reload keeps the loop free of branches)
             const int nx_bh = more ? W.bh : cur_bh;
             const int nx_q0 = more ? W.q0() : cur_q0;
             const float nx_lw = more ? W.lw : cur_lw;
-            fetch(nx_bh, nx_q0, nx_lw, buf ^ 1);
-            const bool mask = (CAUSAL && k0 + kBN - 1 > cur_q0) || (k0 + kBN > N);
-            body(buf, mask);
-            stage(buf ^ 1, nx_lw);
+            // causal: key <= cur_q0 + ql; keys past N are never kept
+            const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
+            const bf16* sq = sQD[buf][0];
+            const bf16* sdo = sQD[buf][1];
+            const float* sl = sLD[buf][0];
+            const float* sd = sLD[buf][1];
+            f32x16 s, dp;
+            bf16x8 pa[2], da[2];
+            auto nothing = [&](int) {};
+            // the next sub-tile's loads go out with this one's first products,
+            // and its Q/dO pieces are stored to LDS during the last softmax
+            sdp(sq, sdo, 0, s, dp, [&]() { fetch(nx_bh, nx_q0, nx_lw, fbuf); });
+            sm_dvdk(with_softmax, s, dp, sl, sd, 0, thr, pa, da, sQD[pbuf][0], sQD[pbuf][1], 1,
+                    ppa, pda, nothing);
+            sdp(sq, sdo, 1, s, dp, []() {});
+            sm_dvdk(with_softmax, s, dp, sl, sd, 1, thr, ppa, pda, sq, sdo, 0, pa, da,
+                    [&](int m) {
+                        if ((m & 1) == 0 && m / 2 < 2 * NPIECE) {
+                            const int pc = m / 2;
+                            if (pc < NPIECE) fq.commit_one(sQD[fbuf][0], wave, lane, pc);
+                            else fo.commit_one(sQD[fbuf][1], wave, lane, pc - NPIECE);
+                        }
+                    });
+            stage_rows(fbuf, nx_lw);
             __syncthreads();
             if (!more) break;
-            buf ^= 1;
+            pbuf = buf;
+            buf = fbuf;
             cur_bh = nx_bh;
             cur_q0 = nx_q0;
             cur_lw = nx_lw;
         }
+        {
+            f32x16 s0 = zero16;
+            bf16x8 ua[2], ub[2];
+            sm_dvdk(no_softmax, s0, s0, sLD[buf][0], sLD[buf][1], 1, 0, ua, ub, sQD[buf][0],
+                    sQD[buf][1], 1, ppa, pda, [](int) {});
+        }
     }
+    // the accumulators were last written by MFMAs the compiler does not see:
+    // give them their result latency before the epilogue reads them
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     // ---- epilogue: dK = scale * acc, dV = acc, bf16
 #pragma unroll
