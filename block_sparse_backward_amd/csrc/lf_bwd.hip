@@ -227,6 +227,7 @@ __device__ __forceinline__ void pipeline_schedule_vmem() {
 // to the next sub-tile costs no memory round trip.
 template <int BLK, bool CAUSAL>
 struct Walk {
+    static_assert(kBN % BLK == 0 && BLK % kBM == 0, "key tiles start on block boundaries");
     const int32_t* kept_idx;
     const int32_t* kept_count;
     const float* block_w;
@@ -237,7 +238,7 @@ struct Walk {
     float vlw;   // log2(block_w[bh][vidx])
 
     __device__ __forceinline__ void load_chunk(int c) {
-        cbase = c;
+        cbase = __builtin_amdgcn_readfirstlane(c);
         const int p = c + lane;
         int idx = 0x7fffffff;
         float w = 1.f;
@@ -250,7 +251,7 @@ struct Walk {
     }
     __device__ __forceinline__ void load_head() {
         bh = b * Hq + g * G + hg;
-        cnt = min(max(kept_count[bh], 0), nqb);
+        cnt = __builtin_amdgcn_readfirstlane(min(max(kept_count[bh], 0), nqb));
         st = 0;
         pos = cnt;
         // first kept block whose rows reach key k0 (all of them when not causal)
@@ -259,7 +260,7 @@ struct Walk {
             load_chunk(c);
             const uint64_t m = __builtin_amdgcn_ballot_w64(vidx >= first_block);
             if (m) {
-                pos = c + __builtin_ctzll(m);
+                pos = __builtin_amdgcn_readfirstlane(c + (int)__builtin_ctzll(m));
                 break;
             }
         }
@@ -293,9 +294,25 @@ struct Walk {
         load_head();
         return settle();
     }
+    // Fast paths first: the next sub-tile of the same block, then the next
+    // kept block of the register chunk.  Neither needs the causal test: the
+    // key tile starts at a multiple of the block size, so every sub-tile of a
+    // block at or after the first one reaching the keys reaches them too.
     __device__ __forceinline__ bool next() {
-        ++st;
-        return settle();
+        if (++st < BLK / kBM) return true;
+        const int np = pos + 1 - cbase;
+        if (pos + 1 < cnt && np < 64) {
+            const int ni = __builtin_amdgcn_readlane(vidx, np);
+            if ((unsigned)ni < (unsigned)nqb) {
+                pos += 1;
+                st = 0;
+                i = ni;
+                lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                   __builtin_bit_cast(int, vlw), np));
+                return true;
+            }
+        }
+        return settle();  // chunk, head or list end, or a malformed entry
     }
     __device__ __forceinline__ int q0() const { return i * BLK + st * kBM; }
 };
