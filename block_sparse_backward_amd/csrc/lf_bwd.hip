@@ -15,26 +15,35 @@
 // The weight is folded into the exponent: exp2(s - (LSE log2 e - log2 w)) =
 // w P, so dS and every product carry it for free.
 //
-// Two kernels, both deterministic (no atomics, no workspace):
+// Two walks, both deterministic (no floating-point atomics; every sum is
+// taken in a fixed order):
 //
 // dkdv_bf16_kernel -- one workgroup of 4 waves per (batch, kv head, 128-key
 //   tile); wave w owns keys 32w..32w+31 and keeps its K/V fragments and its
 //   dK/dV accumulators in registers for the whole walk.  The workgroup walks
 //   the kept blocks of the Hq/Hkv query heads of its group in 64-row
-//   sub-tiles; Q and dO rows go from HBM straight into double-buffered LDS
-//   (buffer loads to LDS) while the previous sub-tile computes.  Per sub-tile,
-//   on 32x32x16 bf16 MFMAs: S = Q K_w^T and dP = dO V_w^T (A: LDS rows, B:
-//   registers), P' and dS' in the accumulator layout, then dV_w += P'^T dO and
-//   dK_w += dS'^T Q (A: P' / dS' straight from the score accumulators, B:
-//   transposing LDS reads of the row-major tiles).
+//   sub-tiles, software-pipelined over three LDS buffers: the next sub-tile's
+//   Q and dO rows are loaded into registers during the current one's first
+//   products and stored to LDS during its last softmax.  On 32x32x16 bf16
+//   MFMAs: S = Q K_w^T and dP = dO V_w^T (A: LDS rows, B: registers), P' and
+//   dS' in the accumulator layout, then dV_w += P'^T dO and dK_w += dS'^T Q
+//   (A: P' / dS' straight from the score accumulators, B: transposing LDS
+//   reads of the row-major tiles), each softmax interleaved with the dV/dK
+//   products of the neighbouring 32-row tile.
 //
-// dq_bf16_kernel -- one workgroup per query block (skipped blocks just write
-//   their zero rows); each wave owns 32 query rows, keeps Q and dO fragments,
-//   its LSE'/D row terms and its dQ accumulator in registers, and walks the
-//   64-key tiles it can see, staged in double-buffered LDS.  Scores are
-//   computed transposed, S^T = K Q^T and dP^T = V dO^T, so dS^T in the
-//   accumulator layout is directly the A operand of dQ += dS K; K^T comes from
-//   transposing LDS reads.  Small enough for two waves per SIMD.
+// dQ: dq_plan_kernel -> dq_bf16_kernel -> dq_finalize_kernel.  The plan lists
+//   the kept blocks longest first (causal blocks see more keys the later they
+//   sit) and, when few blocks are kept, cuts long blocks into chunks of key
+//   steps so the persistent walk is not bound by its longest item; zero-fill
+//   items for the rows of skipped blocks follow.  Each workgroup of the walk
+//   takes items from a queue; its waves own 32 query rows each and keep Q and
+//   dO fragments, the LSE'/D row terms and the dQ accumulator in registers,
+//   while two wave streams take the even and odd 64-key steps staged in
+//   double-buffered LDS.  Scores are computed transposed, S^T = K Q^T and
+//   dP^T = V dO^T, so dS^T in the accumulator layout is directly the A operand
+//   of dQ += dS K; K^T comes from transposing LDS reads.  A one-chunk block
+//   writes its dq rows; chunks write fp32 partials that the finalize pass adds
+//   in chunk order.  The queue position is the only atomic.
 #include "lf_common.h"
 #include "lf_internal.h"
 
@@ -43,7 +52,6 @@ namespace lf {
 constexpr int kBN = 128;  // keys per dK/dV workgroup
 constexpr int kBM = 64;   // query rows per dK/dV sub-tile
 constexpr int kQN = 64;   // keys per dQ step
-constexpr int kBPad = 8;  // bf16 elements of padding per LDS row
 
 __device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int& b, int& g, int& j) {
     const int nG = B * Hkv;
@@ -59,30 +67,6 @@ __device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int& b, i
     }
     b = gid / Hkv;
     g = gid % Hkv;
-}
-
-// Workgroup -> (batch, query head, query block): heads of one kv group on one
-// XCD, largest causal blocks first.
-__device__ __forceinline__ void map_dq_block(int bid, int B, int Hq, int Hkv, int nqb, bool causal,
-                                             int& b, int& h, int& i) {
-    const int G = Hq / Hkv;
-    const int nG = B * Hkv;
-    int tr;
-    if (nG % kNumXcd == 0) {
-        const int xcd = bid % kNumXcd, r = bid / kNumXcd;
-        const int nhx = (nG / kNumXcd) * G;
-        const int hi = r % nhx;
-        tr = r / nhx;
-        const int gid = xcd + kNumXcd * (hi / G);
-        b = gid / Hkv;
-        h = (gid % Hkv) * G + hi % G;
-    } else {
-        const int hi = bid % (B * Hq);
-        tr = bid / (B * Hq);
-        b = hi / Hq;
-        h = hi % Hq;
-    }
-    i = causal ? nqb - 1 - tr : tr;
 }
 
 // LDS tiles are row-major [ROWS][HD] bf16 with no padding; the 16-byte chunk c
@@ -611,24 +595,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
 constexpr int kDqGrid = 256;                 // persistent workgroups (one per CU)
 constexpr int kDqMaxSlots = 6 * kDqGrid;     // fp32 partial tiles, see dq_plan_kernel
 constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
+constexpr int kDqChunkBelow = 2 * kDqGrid;   // chunk blocks when fewer are kept
+constexpr int kDqZeroPer = 8;                // skipped blocks per zero-fill item
+constexpr int kDqFinGrid = 128;              // workgroups of the finalize pass
 
 struct DqWorkspace {  // carved out of the caller's workspace
-    int* ctrl;        // [0] number of items, [1] queue position
-    int4* items;      // {bh, block, first step | end step << 16, partial slot or -1}
+    int* ctrl;        // [0] items, [1] queue position, [2] chunked blocks
+    int4* items;      // compute: {bh, block, first step | end step << 16, partial slot or -1}
+                      // zero fill: {-1, first skipped-list entry, entries, 0}
     int2* blk;        // per (bh, block): {first slot or -1, chunks}
+    int* skip;        // skipped blocks, (bh, block) in memory order
+    int* chunked;     // blocks cut into chunks
     float* part;      // [kDqMaxSlots][BLK * HD]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// compute items: one per kept block, or (chunking) at most 2 T / CL <= kDqMaxSlots
+// chunks plus one per block; zero-fill items: one per kDqZeroPer skipped blocks
 __host__ __device__ inline size_t dq_max_items(size_t nblocks) {
-    return nblocks > (size_t)kDqMaxSlots ? nblocks : (size_t)kDqMaxSlots;
+    return nblocks + (size_t)kDqMaxSlots + nblocks / kDqZeroPer + 1;
 }
 
 __host__ __device__ inline size_t dq_workspace_bytes(size_t nblocks, int blk, int hd) {
     return align256(64 * sizeof(int)) + align256(dq_max_items(nblocks) * sizeof(int4)) +
-           align256(nblocks * sizeof(int2)) +
-           (size_t)kDqMaxSlots * blk * hd * sizeof(float);
+           align256(nblocks * sizeof(int2)) + align256(nblocks * sizeof(int)) +
+           align256(kDqChunkBelow * sizeof(int)) + (size_t)kDqMaxSlots * blk * hd * sizeof(float);
 }
 
 __host__ __device__ inline DqWorkspace dq_workspace(void* base, size_t nblocks, int blk, int hd) {
@@ -640,6 +632,10 @@ __host__ __device__ inline DqWorkspace dq_workspace(void* base, size_t nblocks, 
     p += align256(dq_max_items(nblocks) * sizeof(int4));
     w.blk = reinterpret_cast<int2*>(p);
     p += align256(nblocks * sizeof(int2));
+    w.skip = reinterpret_cast<int*>(p);
+    p += align256(nblocks * sizeof(int));
+    w.chunked = reinterpret_cast<int*>(p);
+    p += align256(kDqChunkBelow * sizeof(int));
     w.part = reinterpret_cast<float*>(p);
     (void)blk;
     (void)hd;
@@ -701,12 +697,12 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
         }
     }
     int K, T;
-    block_scan_1024(kc, sh, &K);
+    const int kpre = block_scan_1024(kc, sh, &K);
     block_scan_1024(ts, sh, &T);
-    const bool chunking = K < 2 * kDqGrid;
+    const bool chunking = K < kDqChunkBelow;
     const int CL = chunking ? max(kDqMinChunk, (T + 4 * kDqGrid - 1) / (4 * kDqGrid)) : (1 << 30);
-    // pass 2: items and partial slots
-    int ni = 0, nsl = 0;
+    // pass 2: compute items, partial slots and chunked blocks per thread
+    int ni = 0, nsl = 0, nck = 0;
     for (int e = e0; e < e1; ++e) {
         int bh, i;
         entry(e, bh, i);
@@ -714,16 +710,20 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
             const int nch = (steps(i) + CL - 1) / CL;
             ni += nch;
             nsl += nch > 1 ? nch : 0;
+            nck += nch > 1;
         }
     }
-    int n_items, n_slots;
+    int n_items, n_slots, n_chunked;
     int it = block_scan_1024(ni, sh, &n_items);
     int sl = block_scan_1024(nsl, sh, &n_slots);
+    int ck = block_scan_1024(nck, sh, &n_chunked);
+    int sk = e0 - kpre;  // skipped blocks before this thread's entries
     for (int e = e0; e < e1; ++e) {
         int bh, i;
         entry(e, bh, i);
+        const int blk = bh * nqb + i;
         int2 info = make_int2(-1, 0);
-        if (block_w[(size_t)bh * nqb + i] != 0.f) {
+        if (block_w[blk] != 0.f) {
             const int L = steps(i);
             const int nch = (L + CL - 1) / CL;
             info = make_int2(nch > 1 ? sl : -1, nch);
@@ -731,13 +731,25 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
                 const int s0 = c * CL, s1 = min(L, s0 + CL);
                 ws.items[it++] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
             }
-            if (nch > 1) sl += nch;
+            if (nch > 1) {
+                sl += nch;
+                ws.chunked[ck++] = blk;
+            }
+        } else {
+            ws.skip[sk++] = blk;
         }
-        ws.blk[(size_t)bh * nqb + i] = info;
+        ws.blk[blk] = info;
     }
+    // zero-fill items go last: they take up the walk's tail
+    const int n_skip = E - K;
+    const int n_zero = (n_skip + kDqZeroPer - 1) / kDqZeroPer;
+    for (int z = tid; z < n_zero; z += 1024)
+        ws.items[n_items + z] =
+            make_int4(-1, z * kDqZeroPer, min(kDqZeroPer, n_skip - z * kDqZeroPer), 0);
     if (tid == 0) {
-        ws.ctrl[0] = n_items;
+        ws.ctrl[0] = n_items + n_zero;
         ws.ctrl[1] = 0;
+        ws.ctrl[2] = n_chunked;
     }
 }
 
@@ -777,6 +789,17 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
         if (t_item >= n_items) break;
         // the item is wave-uniform: keep it in scalar registers
         const int4 item = ws.items[t_item];
+        if (__builtin_amdgcn_readfirstlane(item.x) < 0) {  // zero-fill skipped blocks
+            const int z0 = __builtin_amdgcn_readfirstlane(item.y);
+            const int zn = __builtin_amdgcn_readfirstlane(item.z);
+            for (int zz = 0; zz < zn; ++zz) {
+                const int blk = __builtin_amdgcn_readfirstlane(ws.skip[z0 + zz]);
+                u32x4* dst = reinterpret_cast<u32x4*>(dq + (size_t)blk * BLK * HD);
+#pragma unroll
+                for (int c = 0; c < BLK * HD / 8 / (4 * BLK); ++c) dst[c * 4 * BLK + tid] = u32x4{};
+            }
+            continue;
+        }
         const int bh = __builtin_amdgcn_readfirstlane(item.x);
         const int i = __builtin_amdgcn_readfirstlane(item.y);
         const int st0 = __builtin_amdgcn_readfirstlane(item.z & 0xffff);
@@ -939,36 +962,35 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
     }
 }
 
-// dq rows of every block: zeros for skipped blocks, the in-order sum of the
-// partial slots for chunked blocks; single-chunk blocks were written already.
+// dq rows of the blocks cut into chunks: the in-order sum of their chunk
+// partials (every other block's rows were written by the walk).
 template <int HD, int BLK>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ block_w,
-                                                          DqWorkspace ws, bf16* __restrict__ dq) {
-    const size_t e = blockIdx.x;  // (bh, block) in memory order
-    bf16x4* out = reinterpret_cast<bf16x4*>(dq + e * BLK * HD);
-    if (block_w[e] == 0.f) {
-        for (int c = threadIdx.x; c < BLK * HD / 4; c += 256) out[c] = bf16x4{};
-        return;
-    }
-    const int2 info = ws.blk[e];
-    if (info.x < 0) return;
-    for (int c = threadIdx.x; c < BLK * HD / 4; c += 256) {
-        f32x4 s = reinterpret_cast<const f32x4*>(ws.part + (size_t)info.x * BLK * HD)[c];
-        for (int j = 1; j < info.y; ++j) {
-            const f32x4 x = reinterpret_cast<const f32x4*>(ws.part + (size_t)(info.x + j) * BLK * HD)[c];
-            s += x;
-        }
-        bf16x4 o;
+__global__ __launch_bounds__(256) void dq_finalize_kernel(DqWorkspace ws, bf16* __restrict__ dq) {
+    const int n = ws.ctrl[2];
+    for (int c = blockIdx.x; c < n; c += gridDim.x) {
+        const int e = ws.chunked[c];
+        const int2 info = ws.blk[e];
+        bf16x8* out = reinterpret_cast<bf16x8*>(dq + (size_t)e * BLK * HD);
+        const float* p0 = ws.part + (size_t)info.x * BLK * HD;
+        for (int v = threadIdx.x; v < BLK * HD / 8; v += 256) {
+            f32x4 s0 = reinterpret_cast<const f32x4*>(p0)[2 * v];
+            f32x4 s1 = reinterpret_cast<const f32x4*>(p0)[2 * v + 1];
+            for (int j = 1; j < info.y; ++j) {
+                const float* pj = p0 + (size_t)j * BLK * HD;
+                s0 += reinterpret_cast<const f32x4*>(pj)[2 * v];
+                s1 += reinterpret_cast<const f32x4*>(pj)[2 * v + 1];
+            }
+            bf16x8 o;
 #pragma unroll
-        for (int z = 0; z < 4; ++z) o[z] = to_bf16(s[z]);
-        out[c] = o;
+            for (int z = 0; z < 4; ++z) {
+                o[z] = to_bf16(s0[z]);
+                o[4 + z] = to_bf16(s1[z]);
+            }
+            out[v] = o;
+        }
     }
 }
 
-// ---------------------------------------------------------------------------
-// float32 path: plain loops.
-// dK/dV: one thread per key row; dQ: one thread per query row.
-// ---------------------------------------------------------------------------
 template <int HD>
 __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -1105,8 +1127,8 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
                                (const bf16*)dout, D, block_w, (bf16*)dq, ws, pb.B, pb.Hq,       \
                                pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);                            \
-            hipLaunchKernelGGL((dq_finalize_kernel<DD, BB>), dim3((unsigned)nblocks), dim3(256), \
-                               0, st, block_w, ws, (bf16*)dq);                                  \
+            hipLaunchKernelGGL((dq_finalize_kernel<DD, BB>), dim3(kDqFinGrid), dim3(256), 0, st,  \
+                               ws, (bf16*)dq);                                                  \
         }                                                                                       \
         return hipGetLastError();                                                               \
     }

@@ -145,7 +145,7 @@ lf_status lf_attn_bwd(const lf_shape* shape, const void* q, const void* k, const
 /*
  * Workspace bytes that lf_attn_bwd and lf_attn_bwd_phases need for `shape`
  * (written to *bytes).  It depends on the shape only: at most
- * 6144 * block * head_dim + 24 * B * Hq * nqb + 26 KiB, about 100 MB for
+ * 6144 * block * head_dim + 30 * B * Hq * nqb + 29 KiB, about 100 MB for
  * block = head_dim = 128, and 0 for LF_F32.  Shape errors as in lf_attn_bwd.
  */
 lf_status lf_bwd_workspace_size(const lf_shape* shape, size_t* bytes);
