@@ -91,11 +91,28 @@ __device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t rs, int 
     constexpr int CPR = HD / 8;
     constexpr int NINST = ROWS * CPR / 64;
     static_assert(ROWS * CPR % 64 == 0, "slot layout");
-    for (int m = wave; m < NINST; m += NWAVES) {
-        const int S = 64 * m + lane;
-        const int row = S / CPR, c = (S % CPR) ^ swz<HD>(S / CPR);
-        const int voff = (row * HD + c * 8) * (int)sizeof(bf16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * m), 16, voff, soff, 0, 0);
+    static_assert(NINST % NWAVES == 0, "whole rounds");
+    // rows advance by RS per round; the swizzle repeats every 16 rows, so when
+    // RS is a multiple of 16 one lane offset serves every round and the round
+    // moves the scalar offset
+    constexpr int RS = 64 * NWAVES / CPR;
+    constexpr bool kPeriodic = RS % 16 == 0;
+    const int S0 = 64 * wave + lane;
+    const int voff0 =
+        ((S0 / CPR) * HD + ((S0 % CPR) ^ swz<HD>(S0 / CPR)) * 8) * (int)sizeof(bf16);
+#pragma unroll
+    for (int mm = 0; mm < NINST / NWAVES; ++mm) {
+        const int m = wave + NWAVES * mm;
+        if constexpr (kPeriodic) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * m), 16, voff0,
+                                                     soff + mm * RS * HD * (int)sizeof(bf16), 0, 0);
+        } else {
+            const int S = 64 * m + lane;
+            const int row = S / CPR, c = (S % CPR) ^ swz<HD>(S / CPR);
+            const int voff = (row * HD + c * 8) * (int)sizeof(bf16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + 512 * m), 16, voff, soff,
+                                                     0, 0);
+        }
     }
 }
 
@@ -757,7 +774,13 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
 // two streams of NW waves each (32 query rows per wave) split the steps, even
 // steps to stream 0, odd to stream 1, and add their partials in LDS at the
 // end; the result goes to the dq rows (single-chunk block) or to the item's
-// fp32 partial slot.
+// fp32 partial slot.  Each stream double-buffers its K/V tiles in two LDS
+// arrays of its own, and the code of each stream and buffer names its arrays
+// at compile time: loads to LDS into one array then never hold back the LDS
+// reads of another (the compiler waits for a load to LDS before reading the
+// same array).  The next step's loads go out among the current step's score
+// MFMAs.  Steps run without branches: keys the causal mask hides, and the
+// missing last step of stream 1 when the count is odd, add exact zeros.
 template <int HD, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -767,10 +790,13 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
     constexpr int NW = BLK / 32;
     constexpr int KS = HD / 16;
     constexpr int DT = HD / 32;
-    constexpr int TILE = kQN * HD;     // one staged K or V tile (swizzled)
-    static_assert(BLK * (HD + 4) * sizeof(float) <= sizeof(bf16) * 2 * 2 * 2 * TILE,
-                  "the fp32 dQ tile fits in the K/V staging buffers");
-    __shared__ __attribute__((aligned(16))) bf16 sKV[2][2][2][TILE];   // [stream][buffer][K | V]
+    constexpr int TILE = kQN * HD;  // one staged K or V tile (swizzled)
+    // a stream's fp32 partial (NW waves x 32 rows x HD) fits in its two buffers
+    static_assert(BLK * HD * sizeof(float) <= 2 * 2 * TILE * sizeof(bf16), "epilogue space");
+    __shared__ __attribute__((aligned(16))) bf16 sA0[2 * TILE];  // stream 0: K | V, buffer 0
+    __shared__ __attribute__((aligned(16))) bf16 sA1[2 * TILE];  // stream 0, buffer 1
+    __shared__ __attribute__((aligned(16))) bf16 sB0[2 * TILE];  // stream 1, buffer 0
+    __shared__ __attribute__((aligned(16))) bf16 sB1[2 * TILE];  // stream 1, buffer 1
     __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63, wave_all = tid >> 6;
@@ -808,8 +834,7 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
         const int b = bh / Hq, g = (bh % Hq) / G;
         const size_t qoff = (size_t)bh * N * HD;
         const float lw = __log2f(block_w[(size_t)bh * nqb + i]);
-        const int qw0 = i * BLK + 32 * wave;  // first row of this wave
-        const int qrow = qw0 + l32;           // query column held by this lane
+        const int qrow = i * BLK + 32 * wave + l32;  // query column held by this lane
 
         // Q^T and dO^T fragments (B operands): column = query, k = head dim
         bf16x8 qf[KS], of[KS];
@@ -830,27 +855,27 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)N * HD * sizeof(bf16));
         const int nkt = st1 - st0;
         const int nit = (nkt + 1) / 2;  // iterations: steps 2t (stream 0) and 2t + 1 (stream 1)
-        auto fetch = [&](int t, int BF) {
-            const int kt = 2 * t + stream;
-            if (kt < nkt) {
-                const int soff = (st0 + kt) * kQN * HD * (int)sizeof(bf16);
-                load_tile_to_lds<HD, kQN, NW>(rk, soff, sKV[stream][BF][0], wave, lane);
-                load_tile_to_lds<HD, kQN, NW>(rv, soff, sKV[stream][BF][1], wave, lane);
-            }
-        };
 
-        auto step = [&](int t, int BUF) {
-            if (t + 1 < nit) fetch(t + 1, BUF ^ 1);
-            const int kt = 2 * t + stream;
-            const int k0 = (st0 + kt) * kQN;
-            if (kt < nkt && (!CAUSAL || k0 <= qw0 + 31)) {  // a visible key in this wave's step
-                const bf16* sk = sKV[stream][BUF][0];
-                const bf16* sv = sKV[stream][BUF][1];
-                const bool mask = CAUSAL && k0 + kQN - 1 > qw0;
+        auto walk = [&](auto SC, bf16* buf0, bf16* buf1) {
+            constexpr int S = decltype(SC)::value;
+            // the K and V tiles of iteration t (a step past the end reloads the last)
+            auto fetch = [&](int t, bf16* dst) {
+                const int kt = min(2 * t + S, nkt - 1);
+                const int soff = (st0 + kt) * kQN * HD * (int)sizeof(bf16);
+                load_tile_to_lds<HD, kQN, NW>(rk, soff, dst, wave, lane);
+                load_tile_to_lds<HD, kQN, NW>(rv, soff, dst + TILE, wave, lane);
+            };
+            auto step = [&](int t, const bf16* sk, bf16* nxt) {
+                const int kt = 2 * t + S;
+                const int k0 = (st0 + kt) * kQN;
+                // key kk of this lane's query is kept iff kk <= lim
+                const int lim = kt < nkt ? (CAUSAL ? qrow : 0x7fffffff) : -1;
+                const bf16* sv = sk + TILE;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the step
                     f32x16 s, dp;
                     {
+                        if (mt == 0) fetch(t + 1, nxt);  // issued among the MFMAs below
                         bf16x8 ak[KS], av[KS];
 #pragma unroll
                         for (int ks = 0; ks < KS; ++ks) {
@@ -862,8 +887,10 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
                             s = mfma32(ak[ks], qf[ks], ks ? s : zero16);
                             dp = mfma32(av[ks], of[ks], ks ? dp : zero16);
                         }
-                        pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
+                        if (mt == 0) pipeline_schedule_vmem<2 * KS, 2 * KS, 1, 6, 2 * TILE / (64 * 8 * NW)>();
+                        else pipeline_schedule<2 * KS, 2 * KS, 1, 6>();
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                     // dS'^T = P' (dP - D) in the accumulator layout (row = key, col = query)
                     bf16x8 da[2];
                     {
@@ -871,10 +898,8 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             float p = fast_exp2(s[r] * scale_log2 - lse_l);
-                            if (mask) {
-                                const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                                if (kk > qrow) p = 0.f;
-                            }
+                            const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                            if (kk > lim) p = 0.f;
                             dsv[r] = p * (dp[r] - d_l);
                         }
 #pragma unroll
@@ -900,63 +925,71 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
                                 acc[dt] = mfma32(da[half], kb[half][dt], acc[dt]);
                         pipeline_schedule<4 * DT, 2 * DT, 2, 4>();
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            };
+            fetch(0, buf0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            for (int t = 0; t < nit; t += 2) {
+                step(t, buf0, buf1);
+                if (t + 1 < nit) step(t + 1, buf1, buf0);
+            }
         };
+        if (stream == 0) walk(IntC<0>{}, sA0, sA1);
+        else walk(IntC<1>{}, sB0, sB1);
 
-        fetch(0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        for (int t = 0; t < nit; ++t) step(t, t & 1);
-
-        // Both streams' partials meet in a row-major fp32 tile in LDS (the
-        // staging buffers are free after the last barrier; rows padded by 4
-        // floats so the two half-waves hit different banks): stream 1 stores,
-        // stream 0 adds, then every thread writes 16-byte row pieces.
-        float* red = reinterpret_cast<float*>(&sKV[0][0][0][0]);
-        constexpr int RS = HD + 4;  // row stride of the tile, floats
-        float* rw = red + (32 * wave + 4 * hf) * RS + l32;  // row 4hf, column l32 of this wave
+        // Stream 1 hands its partial to stream 0 through its own two buffers
+        // (lane-major, 16 floats per C tile, one 32 x HD region per wave);
+        // stream 0 adds it, scales, and stages the result row-major in its
+        // buffers for 16-byte writes by every thread.
+        constexpr int WREG = 32 * HD;                     // floats per wave region
+        constexpr int WPB = (2 * TILE * 2) / (WREG * 4);  // wave regions per buffer
+        float* xr = reinterpret_cast<float*>(wave / WPB ? sB1 : sB0) + (wave % WPB) * WREG;
         if (stream == 1) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) rw[(8 * (r >> 2) + (r & 3)) * RS + 32 * dt] = acc[dt][r];
+                for (int r = 0; r < 16; ++r) xr[(dt * 16 + r) * 64 + lane] = acc[dt][r];
         }
         __syncthreads();
+        // row-major staging of the result: rows of wave w at ((w / WPB) ? sA1 : sA0)
+        const int row0 = 4 * hf;  // plus 8 (r >> 2) + (r & 3) within the wave's 32 rows
         if (stream == 0) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) rw[(8 * (r >> 2) + (r & 3)) * RS + 32 * dt] += acc[dt][r];
+                for (int r = 0; r < 16; ++r) acc[dt][r] = (acc[dt][r] + xr[(dt * 16 + r) * 64 + lane]) * scale;
+            if (slot < 0) {  // bf16 rows: all NW waves' rows fit in sA0
+                bf16* ob = sA0 + (32 * wave + row0) * HD + l32;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        ob[(8 * (r >> 2) + (r & 3)) * HD + 32 * dt] = to_bf16(acc[dt][r]);
+            } else {  // fp32 rows: WPB waves per buffer
+                float* of32 = reinterpret_cast<float*>(wave / WPB ? sA1 : sA0) +
+                              ((wave % WPB) * 32 + row0) * HD + l32;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        of32[(8 * (r >> 2) + (r & 3)) * HD + 32 * dt] = acc[dt][r];
+            }
         }
         __syncthreads();
-        // scale * tile -> dq rows (bf16) or the item's partial slot (fp32)
-        constexpr int NV = BLK * HD / 8;  // 8-float pieces
         if (slot < 0) {
             bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
-            for (int c = tid; c < NV; c += 2 * NW * 64) {
-                const int row = c / (HD / 8), col = 8 * (c % (HD / 8));
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(red + row * RS + col);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(red + row * RS + col + 4);
-                bf16x8 o;
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    o[z] = to_bf16(x0[z] * scale);
-                    o[4 + z] = to_bf16(x1[z] * scale);
-                }
-                *reinterpret_cast<bf16x8*>(dq_rows + (size_t)row * HD + col) = o;
-            }
+            for (int c = tid; c < BLK * HD / 8; c += 2 * NW * 64)
+                reinterpret_cast<u32x4*>(dq_rows)[c] = reinterpret_cast<const u32x4*>(sA0)[c];
         } else {
             float* part = ws.part + (size_t)slot * BLK * HD;
-            for (int c = tid; c < NV; c += 2 * NW * 64) {
-                const int row = c / (HD / 8), col = 8 * (c % (HD / 8));
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(red + row * RS + col);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(red + row * RS + col + 4);
-                *reinterpret_cast<f32x4*>(part + (size_t)row * HD + col) = x0 * scale;
-                *reinterpret_cast<f32x4*>(part + (size_t)row * HD + col + 4) = x1 * scale;
-            }
+            constexpr int PB = WPB * WREG / 4;  // 16-byte pieces per buffer
+            for (int c = tid; c < BLK * HD / 4; c += 2 * NW * 64)
+                reinterpret_cast<f32x4*>(part)[c] =
+                    reinterpret_cast<const f32x4*>(c < PB ? sA0 : sA1)[c < PB ? c : c - PB];
         }
         __syncthreads();  // the staging buffers are reused by the next item
     }
