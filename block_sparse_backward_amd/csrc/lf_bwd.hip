@@ -614,7 +614,7 @@ constexpr int kDqMaxSlots = 6 * kDqGrid;     // fp32 partial tiles, see dq_plan_
 constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
 constexpr int kDqChunkBelow = 2 * kDqGrid;   // chunk blocks when fewer are kept
 constexpr int kDqZeroPer = 8;                // skipped blocks per zero-fill item
-constexpr int kDqFinGrid = 128;              // workgroups of the finalize pass
+constexpr int kDqFinSplit = 2;               // finalize workgroups per chunked block
 
 struct DqWorkspace {  // carved out of the caller's workspace
     int* ctrl;        // [0] items, [1] queue position, [2] chunked blocks
@@ -996,31 +996,32 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
 }
 
 // dq rows of the blocks cut into chunks: the in-order sum of their chunk
-// partials (every other block's rows were written by the walk).
+// partials (every other block's rows were written by the walk).  Workgroup
+// kDqFinSplit c + h does part h of the rows of chunked block c; the grid covers
+// the most chunked blocks the plan can list.
 template <int HD, int BLK>
 __global__ __launch_bounds__(256) void dq_finalize_kernel(DqWorkspace ws, bf16* __restrict__ dq) {
-    const int n = ws.ctrl[2];
-    for (int c = blockIdx.x; c < n; c += gridDim.x) {
-        const int e = ws.chunked[c];
-        const int2 info = ws.blk[e];
-        bf16x8* out = reinterpret_cast<bf16x8*>(dq + (size_t)e * BLK * HD);
-        const float* p0 = ws.part + (size_t)info.x * BLK * HD;
-        for (int v = threadIdx.x; v < BLK * HD / 8; v += 256) {
-            f32x4 s0 = reinterpret_cast<const f32x4*>(p0)[2 * v];
-            f32x4 s1 = reinterpret_cast<const f32x4*>(p0)[2 * v + 1];
-            for (int j = 1; j < info.y; ++j) {
-                const float* pj = p0 + (size_t)j * BLK * HD;
-                s0 += reinterpret_cast<const f32x4*>(pj)[2 * v];
-                s1 += reinterpret_cast<const f32x4*>(pj)[2 * v + 1];
-            }
-            bf16x8 o;
-#pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                o[z] = to_bf16(s0[z]);
-                o[4 + z] = to_bf16(s1[z]);
-            }
-            out[v] = o;
+    const int c = blockIdx.x / kDqFinSplit, h = blockIdx.x % kDqFinSplit;
+    if (c >= ws.ctrl[2]) return;
+    const int e = ws.chunked[c];
+    const int2 info = ws.blk[e];
+    constexpr int NV = BLK * HD / 8 / kDqFinSplit;  // 8-element pieces of this workgroup
+    bf16x8* out = reinterpret_cast<bf16x8*>(dq + (size_t)e * BLK * HD) + h * NV;
+    const f32x4* p0 = reinterpret_cast<const f32x4*>(ws.part + (size_t)info.x * BLK * HD) + 2 * h * NV;
+    constexpr size_t PS = (size_t)BLK * HD / 4;  // f32x4 per partial
+    for (int v = threadIdx.x; v < NV; v += 256) {
+        f32x4 s0 = p0[2 * v], s1 = p0[2 * v + 1];
+        for (int j = 1; j < info.y; ++j) {
+            s0 += p0[j * PS + 2 * v];
+            s1 += p0[j * PS + 2 * v + 1];
         }
+        bf16x8 o;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            o[z] = to_bf16(s0[z]);
+            o[4 + z] = to_bf16(s1[z]);
+        }
+        out[v] = o;
     }
 }
 
@@ -1160,7 +1161,8 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
                                (const bf16*)dout, D, block_w, (bf16*)dq, ws, pb.B, pb.Hq,       \
                                pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);                            \
-            hipLaunchKernelGGL((dq_finalize_kernel<DD, BB>), dim3(kDqFinGrid), dim3(256), 0, st,  \
+            hipLaunchKernelGGL((dq_finalize_kernel<DD, BB>), dim3(kDqFinSplit * kDqChunkBelow),   \
+                               dim3(256), 0, st,                                                \
                                ws, (bf16*)dq);                                                  \
         }                                                                                       \
         return hipGetLastError();                                                               \
