@@ -53,14 +53,21 @@ constexpr int kBN = 128;  // keys per dK/dV workgroup
 constexpr int kBM = 64;   // query rows per dK/dV sub-tile
 constexpr int kQN = 64;   // keys per dQ step
 
+// Workgroup -> (batch, kv group, key tile), key tiles in ascending order (the
+// longest causal walks first).  Workgroups are dispatched round-robin over the
+// 8 XCDs; a kv group stays on one XCD for kRotate consecutive key tiles (its
+// kept Q/dO rows are then shared in that XCD's L2) and then moves on to the
+// next XCD, so each XCD gets a share of every group: the groups' kept work
+// differs, and a group pinned to one XCD would leave the others idle.
+constexpr int kRotate = 8;
 __device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int& b, int& g, int& j) {
     const int nG = B * Hkv;
     int gid;
     if (nG % kNumXcd == 0) {
         const int xcd = bid % kNumXcd, r = bid / kNumXcd;
         const int ngx = nG / kNumXcd;
-        gid = xcd + kNumXcd * (r % ngx);
         j = r / ngx;
+        gid = (xcd + j / kRotate) % kNumXcd + kNumXcd * (r % ngx);
     } else {
         gid = bid % nG;
         j = bid / nG;
