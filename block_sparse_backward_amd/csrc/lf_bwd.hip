@@ -777,33 +777,43 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
     }
 }
 
-// Persistent dQ walk.  Each item is one kept block's key steps [s0, s1):
-// two streams of NW waves each (32 query rows per wave) split the steps, even
-// steps to stream 0, odd to stream 1, and add their partials in LDS at the
-// end; the result goes to the dq rows (single-chunk block) or to the item's
-// fp32 partial slot.  Each stream double-buffers its K/V tiles in two LDS
-// arrays of its own, and the code of each stream and buffer names its arrays
-// at compile time: loads to LDS into one array then never hold back the LDS
-// reads of another (the compiler waits for a load to LDS before reading the
-// same array).  The next step's loads go out among the current step's score
-// MFMAs.  Steps run without branches: keys the causal mask hides, and the
-// missing last step of stream 1 when the count is odd, add exact zeros.
+// Persistent dQ walk.  Each item is one kept block's key steps [s0, s1).  A
+// workgroup has 4 waves of 32 query rows: for 128-row blocks one stream of 4
+// waves takes every step (two workgroups per CU); for 64-row blocks two
+// streams of 2 waves split the steps, even to stream 0 and odd to stream 1,
+// and add their partials in LDS at the end.  The result goes to the dq rows
+// (single-chunk block) or to the item's fp32 partial slot.  Each stream
+// double-buffers its K/V tiles in two LDS arrays of its own, and the code of
+// each stream and buffer names its arrays at compile time: loads to LDS into
+// one array then never hold back the LDS reads of another (the compiler waits
+// for a load to LDS before reading the same array).  The next step's loads go
+// out among the current step's score MFMAs.  Steps run without branches: keys
+// the causal mask hides, and a stream's missing last step, add exact zeros.
+template <int BLK>
+struct DqShape {
+    static constexpr int NS = BLK >= 128 ? 1 : 2;  // streams per workgroup
+    static constexpr int NW = BLK / 32;            // waves per stream
+    static constexpr int NT = NS * NW * 64;        // threads per workgroup
+    static constexpr int PER_CU = NS == 1 ? 2 : 1; // workgroups per CU
+};
+
 template <int HD, int BLK, bool CAUSAL>
-__global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
+__global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ Drow,
     const float* __restrict__ block_w, bf16* __restrict__ dq, DqWorkspace ws, int B, int Hq,
     int Hkv, int N, int nqb, float scale, float scale_log2) {
-    constexpr int NW = BLK / 32;
+    constexpr int NS = DqShape<BLK>::NS, NW = DqShape<BLK>::NW, NT = DqShape<BLK>::NT;
+    static_assert(NT == 256, "four waves per workgroup");
     constexpr int KS = HD / 16;
     constexpr int DT = HD / 32;
     constexpr int TILE = kQN * HD;  // one staged K or V tile (swizzled)
     // a stream's fp32 partial (NW waves x 32 rows x HD) fits in its two buffers
-    static_assert(BLK * HD * sizeof(float) <= 2 * 2 * TILE * sizeof(bf16), "epilogue space");
+    static_assert(NW * 32 * HD * sizeof(float) <= 2 * 2 * TILE * sizeof(bf16), "epilogue space");
     __shared__ __attribute__((aligned(16))) bf16 sA0[2 * TILE];  // stream 0: K | V, buffer 0
     __shared__ __attribute__((aligned(16))) bf16 sA1[2 * TILE];  // stream 0, buffer 1
-    __shared__ __attribute__((aligned(16))) bf16 sB0[2 * TILE];  // stream 1, buffer 0
-    __shared__ __attribute__((aligned(16))) bf16 sB1[2 * TILE];  // stream 1, buffer 1
+    __shared__ __attribute__((aligned(16))) bf16 sB0[NS == 2 ? 2 * TILE : 8];  // stream 1, buffer 0
+    __shared__ __attribute__((aligned(16))) bf16 sB1[NS == 2 ? 2 * TILE : 8];  // stream 1, buffer 1
     __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63, wave_all = tid >> 6;
@@ -829,7 +839,7 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
                 const int blk = __builtin_amdgcn_readfirstlane(ws.skip[z0 + zz]);
                 u32x4* dst = reinterpret_cast<u32x4*>(dq + (size_t)blk * BLK * HD);
 #pragma unroll
-                for (int c = 0; c < BLK * HD / 8 / (4 * BLK); ++c) dst[c * 4 * BLK + tid] = u32x4{};
+                for (int c = 0; c < BLK * HD / 8 / NT; ++c) dst[c * NT + tid] = u32x4{};
             }
             continue;
         }
@@ -861,19 +871,19 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)N * HD * sizeof(bf16));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)N * HD * sizeof(bf16));
         const int nkt = st1 - st0;
-        const int nit = (nkt + 1) / 2;  // iterations: steps 2t (stream 0) and 2t + 1 (stream 1)
+        const int nit = (nkt + NS - 1) / NS;  // iterations: step NS t + stream
 
         auto walk = [&](auto SC, bf16* buf0, bf16* buf1) {
             constexpr int S = decltype(SC)::value;
             // the K and V tiles of iteration t (a step past the end reloads the last)
             auto fetch = [&](int t, bf16* dst) {
-                const int kt = min(2 * t + S, nkt - 1);
+                const int kt = min(NS * t + S, nkt - 1);
                 const int soff = (st0 + kt) * kQN * HD * (int)sizeof(bf16);
                 load_tile_to_lds<HD, kQN, NW>(rk, soff, dst, wave, lane);
                 load_tile_to_lds<HD, kQN, NW>(rv, soff, dst + TILE, wave, lane);
             };
             auto step = [&](int t, const bf16* sk, bf16* nxt) {
-                const int kt = 2 * t + S;
+                const int kt = NS * t + S;
                 const int k0 = (st0 + kt) * kQN;
                 // key kk of this lane's query is kept iff kk <= lim
                 const int lim = kt < nkt ? (CAUSAL ? qrow : 0x7fffffff) : -1;
@@ -945,37 +955,44 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
                 if (t + 1 < nit) step(t + 1, buf1, buf0);
             }
         };
-        if (stream == 0) walk(IntC<0>{}, sA0, sA1);
-        else walk(IntC<1>{}, sB0, sB1);
+        if constexpr (NS == 1) {
+            walk(IntC<0>{}, sA0, sA1);
+        } else {
+            if (stream == 0) walk(IntC<0>{}, sA0, sA1);
+            else walk(IntC<1>{}, sB0, sB1);
+        }
 
-        // Stream 1 hands its partial to stream 0 through its own two buffers
-        // (lane-major, 16 floats per C tile, one 32 x HD region per wave);
-        // stream 0 adds it, scales, and stages the result row-major in its
-        // buffers for 16-byte writes by every thread.
         constexpr int WREG = 32 * HD;                     // floats per wave region
         constexpr int WPB = (2 * TILE * 2) / (WREG * 4);  // wave regions per buffer
-        float* xr = reinterpret_cast<float*>(wave / WPB ? sB1 : sB0) + (wave % WPB) * WREG;
-        if (stream == 1) {
+        if constexpr (NS == 2) {
+            // stream 1 hands its partial to stream 0 through its own two buffers
+            // (lane-major, 16 floats per C tile, one region per wave)
+            float* xr = reinterpret_cast<float*>(wave / WPB ? sB1 : sB0) + (wave % WPB) * WREG;
+            if (stream == 1) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xr[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+                    for (int r = 0; r < 16; ++r) xr[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+            }
+            __syncthreads();
+            if (stream == 0) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[dt][r] += xr[(dt * 16 + r) * 64 + lane];
+            }
         }
-        __syncthreads();
-        // row-major staging of the result: rows of wave w at ((w / WPB) ? sA1 : sA0)
+        // stream 0 scales and stages the result row-major in its buffers for
+        // 16-byte writes by every thread
         const int row0 = 4 * hf;  // plus 8 (r >> 2) + (r & 3) within the wave's 32 rows
         if (stream == 0) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[dt][r] = (acc[dt][r] + xr[(dt * 16 + r) * 64 + lane]) * scale;
             if (slot < 0) {  // bf16 rows: all NW waves' rows fit in sA0
                 bf16* ob = sA0 + (32 * wave + row0) * HD + l32;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        ob[(8 * (r >> 2) + (r & 3)) * HD + 32 * dt] = to_bf16(acc[dt][r]);
+                        ob[(8 * (r >> 2) + (r & 3)) * HD + 32 * dt] = to_bf16(acc[dt][r] * scale);
             } else {  // fp32 rows: WPB waves per buffer
                 float* of32 = reinterpret_cast<float*>(wave / WPB ? sA1 : sA0) +
                               ((wave % WPB) * 32 + row0) * HD + l32;
@@ -983,18 +1000,18 @@ __global__ __launch_bounds__(4 * BLK, 2) void dq_bf16_kernel(
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        of32[(8 * (r >> 2) + (r & 3)) * HD + 32 * dt] = acc[dt][r];
+                        of32[(8 * (r >> 2) + (r & 3)) * HD + 32 * dt] = acc[dt][r] * scale;
             }
         }
         __syncthreads();
         if (slot < 0) {
             bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
-            for (int c = tid; c < BLK * HD / 8; c += 2 * NW * 64)
+            for (int c = tid; c < BLK * HD / 8; c += NT)
                 reinterpret_cast<u32x4*>(dq_rows)[c] = reinterpret_cast<const u32x4*>(sA0)[c];
         } else {
             float* part = ws.part + (size_t)slot * BLK * HD;
             constexpr int PB = WPB * WREG / 4;  // 16-byte pieces per buffer
-            for (int c = tid; c < BLK * HD / 4; c += 2 * NW * 64)
+            for (int c = tid; c < BLK * HD / 4; c += NT)
                 reinterpret_cast<f32x4*>(part)[c] =
                     reinterpret_cast<const f32x4*>(c < PB ? sA0 : sA1)[c < PB ? c : c - PB];
         }
@@ -1164,7 +1181,8 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
         if (do_q) {                                                                             \
             hipLaunchKernelGGL((dq_plan_kernel<BB>), dim3(1), dim3(1024), 0, st, block_w,       \
                                pb.B * pb.Hq, pb.nqb, pb.N, pb.causal, ws);                      \
-            hipLaunchKernelGGL((dq_bf16_kernel<DD, BB, CC>), dim3(kDqGrid), dim3(4 * BB), 0, st, \
+            hipLaunchKernelGGL((dq_bf16_kernel<DD, BB, CC>),                                     \
+                               dim3(kDqGrid * DqShape<BB>::PER_CU), dim3(DqShape<BB>::NT), 0, st, \
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
                                (const bf16*)dout, D, block_w, (bf16*)dq, ws, pb.B, pb.Hq,       \
                                pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);                            \
