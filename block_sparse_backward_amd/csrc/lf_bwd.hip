@@ -617,7 +617,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
 // blocks first.
 // ---------------------------------------------------------------------------
 constexpr int kDqGrid = 256;                 // persistent workgroups (one per CU)
-constexpr int kDqMaxSlots = 6 * kDqGrid;     // fp32 partial tiles, see dq_plan_kernel
+constexpr int kDqChunkItems = 4 * kDqGrid;   // chunking aims at about this many chunks
+constexpr int kDqMaxSlots = kDqChunkItems + 2 * kDqGrid;  // fp32 partial tiles, see dq_plan_kernel
 constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
 constexpr int kDqChunkBelow = 2 * kDqGrid;   // chunk blocks when fewer are kept
 constexpr int kDqZeroPer = 8;                // skipped blocks per zero-fill item
@@ -697,10 +698,16 @@ __device__ __forceinline__ int block_scan_1024(int x, int* sh, int* total) {
 // One workgroup of 1024 threads.  Entries e = 0 .. E-1 run over (block i
 // descending, head bh ascending); an entry is kept when its block weight is
 // non-zero.  Emits the items in that order and the per-block slot table.
+// Chunk lengths never exceed this many key steps: chunking happens with fewer
+// than kDqChunkBelow kept blocks of at most 8192 steps, cut into T / kDqChunkItems
+// step pieces or longer.
+constexpr int kDqMaxChunk = ((kDqChunkBelow - 1) * 8192 + kDqChunkItems - 1) / kDqChunkItems;
+
 template <int BLK>
 __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__ block_w, int BHq,
                                                        int nqb, int N, int causal, DqWorkspace ws) {
     __shared__ int sh[32];
+    __shared__ int bucket[kDqMaxChunk + 1];  // chunk count, then next queue position, per length
     const int E = BHq * nqb;
     const int tid = threadIdx.x;
     const int per = (E + 1023) / 1024;
@@ -724,7 +731,7 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
     const int kpre = block_scan_1024(kc, sh, &K);
     block_scan_1024(ts, sh, &T);
     const bool chunking = K < kDqChunkBelow;
-    const int CL = chunking ? max(kDqMinChunk, (T + 4 * kDqGrid - 1) / (4 * kDqGrid)) : (1 << 30);
+    const int CL = chunking ? max(kDqMinChunk, (T + kDqChunkItems - 1) / kDqChunkItems) : (1 << 30);
     // pass 2: compute items, partial slots and chunked blocks per thread
     int ni = 0, nsl = 0, nck = 0;
     for (int e = e0; e < e1; ++e) {
@@ -741,6 +748,40 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
     int it = block_scan_1024(ni, sh, &n_items);
     int sl = block_scan_1024(nsl, sh, &n_slots);
     int ck = block_scan_1024(nck, sh, &n_chunked);
+    if (chunking) {
+        // Queue order longest first over all chunks (not block by block): a
+        // counting sort by chunk length, so short remainders end the queue.
+        for (int c = tid; c <= CL; c += 1024) bucket[c] = 0;
+        __syncthreads();
+        for (int e = e0; e < e1; ++e) {
+            int bh, i;
+            entry(e, bh, i);
+            if (block_w[(size_t)bh * nqb + i] != 0.f) {
+                const int L = steps(i);
+                for (int s0 = 0; s0 < L; s0 += CL) atomicAdd(&bucket[min(CL, L - s0)], 1);
+            }
+        }
+        __syncthreads();
+        // exclusive prefix over lengths, longest first: bucket[len] = first
+        // queue position of its chunks
+        constexpr int PER = (kDqMaxChunk + 1 + 1023) / 1024;
+        int cnt[PER], tot = 0;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int len = CL - (tid * PER + u);
+            cnt[u] = len >= 1 ? bucket[len] : 0;
+            tot += cnt[u];
+        }
+        int all;
+        int run = block_scan_1024(tot, sh, &all);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int len = CL - (tid * PER + u);
+            if (len >= 1) bucket[len] = run;
+            run += cnt[u];
+        }
+        __syncthreads();
+    }
     int sk = e0 - kpre;  // skipped blocks before this thread's entries
     for (int e = e0; e < e1; ++e) {
         int bh, i;
@@ -753,7 +794,8 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
             info = make_int2(nch > 1 ? sl : -1, nch);
             for (int c = 0; c < nch; ++c) {
                 const int s0 = c * CL, s1 = min(L, s0 + CL);
-                ws.items[it++] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
+                const int at = chunking ? atomicAdd(&bucket[s1 - s0], 1) : it++;
+                ws.items[at] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
             }
             if (nch > 1) {
                 sl += nch;
