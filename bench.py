@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--delta", type=float, default=None, help="main delta (default 0.1)")
     ap.add_argument("--sweep-steps", type=int, default=5,
                     help="steps per extra delta of the sweep (0: no sweep)")
+    ap.add_argument("--train-steps", type=int, default=5,
+                    help="timed steps of the autograd training step per delta (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds spent on the oracle baseline sample")
@@ -210,6 +212,10 @@ def main():
     others["select_mass_pass"]["achieved_incl_tau"] = round(
         others["select_mass_pass"]["bytes_per_launch"] / (t_sel * 1e-3) / 1e9, 1)
 
+    training = None
+    if args.train_steps > 0:
+        training = training_step_report(cfg, q, k, v, do, main_delta, args.train_steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, main_delta, args.cpu_budget_s, metrics)
@@ -248,6 +254,7 @@ def main():
         "fwd_plus_bwd_speedup_vs_own_dense": (
             round((t_fwd + dense_ms) / (t_fwd + t_attn_bwd), 3) if dense_ms else None),
         "delta_sweep": sweep_out,
+        "training_step": training,
         "roofline": roofline,
         "bwd_walks": bwd_walks,
         "other_kernels": others,
@@ -256,6 +263,54 @@ def main():
                   "ms_per_step is host wall time of whole steps (fwd+select+bwd)",
     }
     print(json.dumps(out), flush=True)
+
+
+def training_step_report(cfg, q, k, v, do, delta, steps):
+    """One attention layer's training step as a user runs it: the autograd
+    wrapper's forward, then o.backward(dO) (selection + sparse backward, a new
+    draw seed per step), against the same step at delta = 0 (every block kept:
+    the dense backward through the same kernels).  The forward is dense in
+    both, which caps the step's speedup at (t_fwd + t_bwd_dense) / t_fwd."""
+    import numpy as np
+    import torch
+
+    from block_sparse_backward_amd.autograd import draw_seed, lazyflash_attention
+
+    stream = torch.cuda.current_stream()
+    leaves = [t.detach().clone().requires_grad_(True) for t in (q, k, v)]
+
+    def run(dl, first_step, n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for i in range(n):
+            for t in leaves:
+                t.grad = None
+            ev[i][0].record(stream)
+            o = lazyflash_attention(*leaves, dl, draw_seed(first_step + i), causal=cfg.causal,
+                                    scale=cfg.scale, block=cfg.block)
+            ev[i][1].record(stream)
+            o.backward(do)
+            ev[i][2].record(stream)
+            del o
+        torch.cuda.synchronize()
+        return np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev])
+
+    res = {}
+    for dl in (delta, 0.0):
+        log(f"[bench] training step (autograd) delta={dl}")
+        run(dl, 1000, 2)
+        res[dl] = run(dl, 0, steps).mean(axis=0)
+    (f_s, b_s), (f_d, b_d) = res[delta], res[0.0]
+    return {"delta": delta, "steps": steps,
+            "fwd_ms": round(float(f_s), 4), "bwd_ms": round(float(b_s), 4),
+            "step_ms": round(float(f_s + b_s), 4),
+            "dense_fwd_ms": round(float(f_d), 4), "dense_bwd_ms": round(float(b_d), 4),
+            "dense_step_ms": round(float(f_d + b_d), 4),
+            "bwd_speedup": round(float(b_d / b_s), 3),
+            "step_speedup": round(float((f_d + b_d) / (f_s + b_s)), 3),
+            "amdahl_bound": round(float((f_d + b_d) / f_d), 3),
+            "note": "block_sparse_backward_amd.autograd.lazyflash_attention forward + "
+                    "o.backward(dO); bwd includes selection; the dense forward bounds the "
+                    "step speedup at amdahl_bound"}
 
 
 def cpu_baseline(cfg, inp, delta, budget_s, metrics):

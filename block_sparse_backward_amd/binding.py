@@ -102,6 +102,9 @@ def _need(t, name, shape, dtype, device):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (the library takes device pointers), "
+                         f"got one on {t.device}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:

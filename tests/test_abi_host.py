@@ -8,6 +8,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from block_sparse_backward_amd import binding as bd
 
@@ -169,3 +170,25 @@ def test_workspace_size_and_checks():
     assert b"workspace" in lib.lf_last_error()
     assert _bwd(lib, shp, ws_bytes=n - 1) == bd.LF_EINVAL
     assert b"workspace" in lib.lf_last_error()
+
+
+def test_draw_seed_is_distinct_and_bounded():
+    from block_sparse_backward_amd.autograd import draw_seed
+    seeds = {draw_seed(s, l, b) for b in (0, 5) for s in (0, 1, 2**32 - 1) for l in (0, 1, 2**16 - 1)}
+    assert len(seeds) == 18 and all(0 <= s < 2**64 for s in seeds)
+    for bad in ((-1, 0, 0), (2**32, 0, 0), (0, 2**16, 0), (0, 0, 2**16)):
+        with pytest.raises(ValueError):
+            draw_seed(*bad)
+
+
+def test_wrapper_and_binding_reject_host_tensors():
+    # Host pointers never reach the library: the binding checks the device
+    # before any call.
+    from block_sparse_backward_amd.autograd import lazyflash_attention
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lazyflash_attention(q, q, q, 0.1, 0, block=64)
+    with pytest.raises(ValueError, match="delta"):
+        lazyflash_attention(q, q, q, 1.0, 0, block=64)
+    with pytest.raises(ValueError, match="delta"):
+        lazyflash_attention(q, q, q, float("nan"), 0, block=64)
