@@ -7,31 +7,36 @@
 // traffic and stays exact (FlashAttention course page on voce.life, section
 // "Le mécanisme").
 //
-// bf16 kernel (gfx950): one workgroup = 4 waves = 128 query rows of one head;
-// each wave owns 32 rows and walks 64-key tiles staged in LDS.  Scores are
-// computed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMAs, so that:
-//   * each lane holds one query column: the row max and row sum of the online
-//     softmax are in-lane reductions plus one exchange with lane l ^ 32;
-//   * P^T in the accumulator layout is directly the B operand of
-//     O^T += V^T P^T (the key order inside a 16-key step is permuted the same
-//     way on both operands);
-//   * V^T fragments come from the row-major V tile by transposing LDS reads.
+// bf16 kernel (gfx950): one workgroup = 4 waves = 128 query rows of one head,
+// two workgroups per CU.  Each wave owns 32 rows and walks 64-key tiles of K
+// and V, double-buffered in LDS (swizzled; loaded straight from HBM with
+// buffer loads to LDS, the next tile's loads issued among the current tile's
+// score MFMAs), one barrier per tile.  The two waves that share a SIMD belong
+// to different workgroups, so one's softmax runs while the other's MFMAs do.
+// On 32x32x16 bf16 MFMAs, per tile and wave:
+//   * S^T = K Q^T (A: K rows from LDS, B: Q^T in registers), so each lane holds
+//     one query column: the row max is an in-lane max3 chain plus one
+//     lane-half swap;
+//   * P^T = exp2(S^T scale log2 e - m) in the accumulator layout is directly
+//     the B operand of O^T += V^T P^T (the key order inside a 16-key step is
+//     permuted the same way on both operands); V^T fragments come from
+//     transposing LDS reads.
+// The running max m is raised only when a tile's max exceeds it by more than
+// 8 (log2 units), so P stays below 2^8 and the rescale of O and l (a rare
+// branch) is skipped on almost every tile; O / l and m + log2 l are exact
+// whatever m is.
+// A negative softmax scale is applied by negating Q (exact in bf16), so the
+// max of the raw scores is the max of the scaled ones.
 // The float32 kernel is a plain per-row loop (small problems, exactness).
 #include "lf_common.h"
 #include "lf_internal.h"
+#include "lf_tile.h"
 
 namespace lf {
 
-constexpr int kFwdBM = 128;  // query rows per workgroup
+constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // keys per tile
-constexpr int kPad = 8;      // bf16 elements of padding per LDS row
-
-template <int HD>
-struct FwdTile {
-    static constexpr int LD = HD + kPad;            // LDS row stride (elements)
-    static constexpr int CHUNKS = kFwdBN * HD / 8;  // 16-byte chunks per tile
-    static constexpr int PER_THREAD = CHUNKS / 256;
-};
+constexpr float kMaxSlack = 8.f;  // log2 units the running max may trail a tile's max
 
 __device__ __forceinline__ void map_fwd_block(int bid, int B, int Hq, int Hkv, int nqt, bool causal,
                                               int& b, int& h, int& t) {
@@ -55,18 +60,36 @@ __device__ __forceinline__ void map_fwd_block(int bid, int B, int Hq, int Hkv, i
     t = causal ? nqt - 1 - tr : tr;  // longest causal rows first
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// S^T (+)= K Q^T step with the score accumulator in VGPRs (the softmax reads
+// it).  The caller waits out the result latency (mfma_result_wait) before any
+// VALU read of the scores.
+__device__ __forceinline__ void mfma_kq(f32x16& s, bf16x8 kf, bf16x8 qf, bool first) {
+    if (first)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(kf), "v"(qf));
+    else
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(kf), "v"(qf));
+}
+__device__ __forceinline__ void mfma_result_wait(f32x16& s) {
+    asm volatile("s_nop 7\n\ts_nop 4" : "+v"(s));
+}
+
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(const bf16* __restrict__ q,
-                                                       const bf16* __restrict__ k,
-                                                       const bf16* __restrict__ v,
-                                                       bf16* __restrict__ o,
-                                                       float* __restrict__ lse, int B, int Hq,
-                                                       int Hkv, int N, float scale_log2) {
-    using TL = FwdTile<HD>;
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict__ q,
+                                                          const bf16* __restrict__ k,
+                                                          const bf16* __restrict__ v,
+                                                          bf16* __restrict__ o,
+                                                          float* __restrict__ lse, int B, int Hq,
+                                                          int Hkv, int N, float cl2, int neg) {
     constexpr int KS = HD / 16;  // k-steps over the head dim
     constexpr int DT = HD / 32;  // 32-wide d tiles of O^T
-    __shared__ __attribute__((aligned(16))) bf16 sK[kFwdBN * TL::LD];
-    __shared__ __attribute__((aligned(16))) bf16 sV[kFwdBN * TL::LD];
+    constexpr int TILE = kFwdBN * HD;
+    constexpr int NLOAD = 2 * TILE / (64 * 8 * 4);  // buffer loads per wave per tile
+    __shared__ __attribute__((aligned(16))) bf16 sK0[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sV0[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sK1[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sV1[TILE];
 
     const int nqt = (N + kFwdBM - 1) / kFwdBM;
     int b, h, t;
@@ -75,141 +98,167 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const bf16* __restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
     const int q0 = t * kFwdBM;
-    const int qw0 = q0 + 32 * wave;      // first row of this wave
-    const int qrow = qw0 + l32;          // query column held by this lane
-    const bool row_ok = qrow < N;
+    const int qw0 = q0 + 32 * wave;  // first row of this wave
+    const int qrow = qw0 + l32;      // query column held by this lane
+    const int lim = CAUSAL ? qrow : 0x7fffffff;  // keys past lim are hidden
 
     const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * HD;
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
-    const bf16* kg = k + kvoff;
-    const bf16* vg = v + kvoff;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)N * HD * sizeof(bf16));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)N * HD * sizeof(bf16));
 
-    // Q^T fragments (B operand): column = query, k = head dim.
+    // Q^T fragments (B operands): column = query, k = head dim; rows past N are 0
     bf16x8 qf[KS];
     {
-        const bf16* qr = q + qoff + (size_t)(row_ok ? qrow : 0) * HD;
+        const bool ok = qrow < N;
+        const bf16* qp = q + qoff + (size_t)(ok ? qrow : 0) * HD + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(qr + 16 * ks + 8 * hf);
-            if (!row_ok) qf[ks] = bf16x8{};
+            u32x4 x = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+            if (!ok) x = u32x4{};
+            if (neg) x ^= 0x80008000u;
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
 
-    f32x16 acc_o[DT];
+    f32x16 acc[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x16{};
-    float m_run = -__builtin_inf(), l_run = 0.f;
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+    float m_use = -__builtin_inf(), l_run = 0.f;
 
     const int last_row = min(q0 + kFwdBM, N) - 1;
-    const int nkt_all = (N + kFwdBN - 1) / kFwdBN;
-    const int nkt = CAUSAL ? min(nkt_all, last_row / kFwdBN + 1) : nkt_all;
+    const int nkt = CAUSAL ? last_row / kFwdBN + 1 : N / kFwdBN;  // N is a multiple of 64
+    // tiles whose keys every row of the workgroup sees
+    const int nfull = CAUSAL ? min(q0 / kFwdBN, nkt) : nkt;
+    const TileOffsets<HD> off(lane);
 
-    // register prefetch of one K and one V tile
-    u32x4 pk[TL::PER_THREAD], pv[TL::PER_THREAD];
-    auto fetch = [&](int kt) {
-#pragma unroll
-        for (int c = 0; c < TL::PER_THREAD; ++c) {
-            const int chunk = tid + 256 * c;
-            const int row = chunk / (HD / 8), col = (chunk % (HD / 8)) * 8;
-            const int key = kt * kFwdBN + row;
-            if (key < N) {
-                pk[c] = *reinterpret_cast<const u32x4*>(kg + (size_t)key * HD + col);
-                pv[c] = *reinterpret_cast<const u32x4*>(vg + (size_t)key * HD + col);
-            } else {
-                pk[c] = u32x4{};
-                pv[c] = u32x4{};
-            }
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int c = 0; c < TL::PER_THREAD; ++c) {
-            const int chunk = tid + 256 * c;
-            const int row = chunk / (HD / 8), col = (chunk % (HD / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&sK[row * TL::LD + col]) = pk[c];
-            *reinterpret_cast<u32x4*>(&sV[row * TL::LD + col]) = pv[c];
-        }
+    auto fetch = [&](int kt, bf16* dk, bf16* dv) __attribute__((always_inline)) {
+        const int soff = kt * kFwdBN * HD * (int)sizeof(bf16);
+        load_tile_to_lds<HD, kFwdBN, 4>(rk, soff, dk, wave, lane);
+        load_tile_to_lds<HD, kFwdBN, 4>(rv, soff, dv, wave, lane);
     };
 
-    fetch(0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        stage();
-        __syncthreads();
-        if (kt + 1 < nkt) fetch(kt + 1);
+    // One 64-key tile: issue the next tile's loads into the other buffer (past
+    // the end: the last tile again), then S^T, softmax, O^T += V^T P^T.
+    // MASK: some keys of the tile are hidden from some rows of the wave.
+    auto tile = [&](auto MASKC, int kt, const bf16* sk, const bf16* sv, int kn, bf16* nk,
+                    bf16* nv) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(MASKC)::value;
         const int k0 = kt * kFwdBN;
-        const bool wave_active = !CAUSAL || k0 <= qw0 + 31;
-        if (wave_active) {
-            // S^T = K Q^T : two 32-key tiles
-            f32x16 s[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                s[mt] = f32x16{};
-                const bf16* arow = &sK[(32 * mt + l32) * TL::LD + 8 * hf];
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    s[mt] = mfma32(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qf[ks], s[mt]);
-            }
-            const bool need_mask = (CAUSAL && k0 + kFwdBN - 1 > qw0) || (k0 + kFwdBN > N);
-            float mx = -__builtin_inf();
+        f32x16 s[2];
+        {
+            fetch(kn, nk, nv);
+            bf16x8 kf[2][KS];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[mt][r] * scale_log2;
-                    if (need_mask) {
-                        const int key = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if (key >= N || (CAUSAL && key > qrow)) x = -__builtin_inf();
-                    }
-                    s[mt][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -__builtin_inf()) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            float ls = 0.f;
-            bf16x8 pb[4];
+                for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = frag_at<HD>(sk, 32 * mt, off.frag[ks]);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                float p[16];
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    p[r] = fast_exp2(s[mt][r] - m_use);
-                    ls += p[r];
-                }
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    bf16x8 f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) f[j] = to_bf16(p[8 * half + j]);
-                    pb[2 * mt + half] = f;
-                }
-            }
-            ls += __shfl_xor(ls, 32);
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
-            // O^T += V^T P^T : A = V^T via transposing reads of the row-major V tile.
-            const int G16 = lane >> 4, j16 = lane & 15;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int rbase = 16 * ks + 4 * (G16 >> 1) + (j16 >> 2);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int col = 32 * dt + 16 * (G16 & 1) + 4 * (j16 & 3);
-                    const bf16x4 lo = lds_read_tr(&sV[rbase * TL::LD + col]);
-                    const bf16x4 hi = lds_read_tr(&sV[(rbase + 8) * TL::LD + col]);
-                    acc_o[dt] = mfma32(cat(lo, hi), pb[ks], acc_o[dt]);
-                }
-            }
+                for (int ks = 0; ks < KS; ++ks) mfma_kq(s[mt], kf[mt][ks], qf[ks], ks == 0);
         }
+        mfma_result_wait(s[0]);
+        mfma_result_wait(s[1]);
+        // softmax over the tile's 64 keys; register r of s[mt] holds key
+        // k0 + 32 mt + 8 (r >> 2) + 4 hf + (r & 3)
+        const int lk = lim - k0 - 4 * hf;
+        if constexpr (MASK) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * mt + 8 * (r >> 2) + (r & 3) > lk) s[mt][r] = -__builtin_inf();
+        }
+        float mx = __builtin_fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+        for (int j = 2; j < 32; j += 2)
+            mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[j >> 4][j & 15]), s[j >> 4][(j & 15) + 1]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        const float m = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cl2;
+        const float m_new = m > m_use + kMaxSlack ? m : m_use;
+        const float alpha = m_new == m_use ? 1.f : fast_exp2(m_use - m_new);
+        m_use = m_new;
+        l_run *= alpha;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float p2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * j + e;
+                    float x = fast_exp2(__builtin_fmaf(s[mt][r], cl2, -m_new));
+                    if constexpr (MASK)
+                        if (32 * mt + 8 * (r >> 2) + (r & 3) > lk) x = 0.f;
+                    p2[e] = x;
+                }
+                pb[2 * mt + (j >> 2)][2 * (j & 3)] = to_bf16(p2[0]);
+                pb[2 * mt + (j >> 2)][2 * (j & 3) + 1] = to_bf16(p2[1]);
+                l_run += p2[0] + p2[1];
+                // keep the sum here: the compiler would otherwise sink the chain
+                // (and every P it reads) to the end of the loop body
+                asm volatile("" : "+v"(l_run));
+            }
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            // the factor passes through the asm so that the products cannot be
+            // hoisted out of the branch (they are the identity when no lane needs them)
+            float a = alpha;
+            asm volatile("" : "+v"(a));
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= a;
+        }
+        // O^T += V^T P^T over the tile's four 16-key steps
+        {
+            bf16x8 vf[4][DT];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vf[ks][dt] = tr_at<HD>(sv, 16 * ks, off.tr[dt]);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vf[ks][dt], pb[ks], acc[dt]);
+            pipeline_schedule<8 * DT, 4 * DT, 2, 8>();
+        }
+    };
+    auto sync = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+    // a tile of the causal tail: masked, plain or hidden for this wave
+    auto tail_tile = [&](int kt, const bf16* sk, const bf16* sv, int kn, bf16* nk, bf16* nv)
+        __attribute__((always_inline)) {
+        const int k0 = kt * kFwdBN;
+        if (k0 + kFwdBN - 1 <= qw0) tile(IntC<0>{}, kt, sk, sv, kn, nk, nv);
+        else if (k0 <= qw0 + 31) tile(IntC<1>{}, kt, sk, sv, kn, nk, nv);
+        else fetch(kn, nk, nv);  // no row of this wave sees these keys
+    };
+
+    fetch(0, sK0, sV0);
+    sync();
+    int kt = 0;
+    for (; kt + 2 <= nfull; kt += 2) {
+        tile(IntC<0>{}, kt, sK0, sV0, kt + 1, sK1, sV1);
+        sync();
+        tile(IntC<0>{}, kt + 1, sK1, sV1, min(kt + 2, nkt - 1), sK0, sV0);
+        sync();
+    }
+    for (; kt < nkt; ++kt) {
+        const int kn = min(kt + 1, nkt - 1);
+        if (kt & 1) tail_tile(kt, sK1, sV1, kn, sK0, sV0);
+        else tail_tile(kt, sK0, sV0, kn, sK1, sV1);
+        sync();
     }
 
-    // epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2
-    if (row_ok) {
-        const float inv = 1.f / l_run;
+    // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 (l summed over the lane pair)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                     false, false);
+    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (qrow < N) {
+        const float inv = 1.f / l;
         bf16* orow = o + qoff + (size_t)qrow * HD;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -217,10 +266,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(const bf16* __restrict__ 
             for (int a = 0; a < 4; ++a) {
                 bf16x4 w;
 #pragma unroll
-                for (int bb = 0; bb < 4; ++bb) w[bb] = to_bf16(acc_o[dt][4 * a + bb] * inv);
+                for (int bb = 0; bb < 4; ++bb) w[bb] = to_bf16(acc[dt][4 * a + bb] * inv);
                 *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hf) = w;
             }
-        if (hf == 0) lse[((size_t)b * Hq + h) * N + qrow] = (m_run + __log2f(l_run)) * kLn2;
+        if (hf == 0) lse[((size_t)b * Hq + h) * N + qrow] = (m_use + __log2f(l)) * kLn2;
     }
 }
 
@@ -286,12 +335,13 @@ hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const voi
     }
     const int nqt = (pb.N + kFwdBM - 1) / kFwdBM;
     dim3 grid((unsigned)(nqt * pb.B * pb.Hq));
-    const float sl2 = pb.scale * kLog2e;
+    const float sl2 = __builtin_fabsf(pb.scale) * kLog2e;
+    const int neg = pb.scale < 0.f;
 #define LF_FWD(DD, CC)                                                                         \
     if (pb.d == DD && (pb.causal != 0) == CC) {                                                \
         hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC>), grid, dim3(256), 0, st, (const bf16*)q,  \
                            (const bf16*)k, (const bf16*)v, (bf16*)o, lse, pb.B, pb.Hq, pb.Hkv, \
-                           pb.N, sl2);                                                         \
+                           pb.N, sl2, neg);                                                    \
         return hipGetLastError();                                                              \
     }
     LF_FWD(64, true)
