@@ -103,27 +103,34 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def run_steps(delta, seeds):
-        """Runs one step per seed; returns per-step event pairs and selections."""
+        """One step per seed: the forwards first, then the backward steps
+        (selection, dK/dV walk, dQ walk) back to back, as in a training step
+        whose backward pass runs over the layers after the forward pass.
+        Returns the wall time, per-step phase times and the selections."""
         sels = [bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev) for _ in seeds]
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in seeds]
+        evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in seeds]
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in seeds]
+        common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv),
+                      workspace=ws)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        for seed, sel, ev in zip(seeds, sels, evs):
+        for ev in evf:
             ev[0].record(stream)
             bd.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, block=cfg.block, out=(o, lse))
             ev[1].record(stream)
+        for seed, sel, ev in zip(seeds, sels, evb):
+            ev[0].record(stream)
             bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
                             scale=cfg.scale, heads_kv=cfg.Hkv, out=sel)
-            ev[2].record(stream)
-            common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv),
-                          workspace=ws)
+            ev[1].record(stream)
             bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DKDV, **common)
-            ev[3].record(stream)
+            ev[2].record(stream)
             bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DQ, **common)
-            ev[4].record(stream)
+            ev[3].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
+        ms = np.array([[f[0].elapsed_time(f[1])] + [e[i].elapsed_time(e[i + 1]) for i in range(3)]
+                       for f, e in zip(evf, evb)])
         flops = [metrics.bwd_flops_kept(s["block_w"].cpu().numpy(), cfg.N, cfg.d, cfg.block,
                                         cfg.causal) for s in sels]
         kept = [float((s["block_w"] != 0).float().mean().item()) for s in sels]
@@ -259,8 +266,10 @@ def main():
         "bwd_walks": bwd_walks,
         "other_kernels": others,
         "cpu_baseline": cpu,
-        "timing": "HIP events on the launch stream, steady state (caches not flushed); "
-                  "ms_per_step is host wall time of whole steps (fwd+select+bwd)",
+        "timing": "HIP events on the launch stream, steady state (caches not flushed); the "
+                  "steps' forwards run first, then their select+bwd back to back (a training "
+                  "step's backward pass follows the whole forward pass); ms_per_step is host "
+                  "wall time of both loops per step",
     }
     print(json.dumps(out), flush=True)
 

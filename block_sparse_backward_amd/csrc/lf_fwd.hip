@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
     int b, h, t;
     map_fwd_block(blockIdx.x, B, Hq, Hkv, nqt, CAUSAL, b, h, t);
     const int g = h / (Hq / Hkv);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
     const int l32 = lane & 31, hf = lane >> 5;
     const int q0 = t * kFwdBM;
     const int qw0 = q0 + 32 * wave;  // first row of this wave
@@ -138,70 +139,68 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
         load_tile_to_lds<HD, kFwdBN, 4>(rv, soff, dv, wave, lane);
     };
 
-    // One 64-key tile: issue the next tile's loads into the other buffer (past
-    // the end: the last tile again), then S^T, softmax, O^T += V^T P^T.
-    // MASK: some keys of the tile are hidden from some rows of the wave.
-    auto tile = [&](auto MASKC, int kt, const bf16* sk, const bf16* sv, int kn, bf16* nk,
-                    bf16* nv) __attribute__((always_inline)) {
+    // Softmax of one 32-key half of a tile (s: the half's S^T accumulator,
+    // register r holding key kh + 8 (r >> 2) + 4 hf + (r & 3)), cut into the
+    // NSL slices that the tile spreads over the MFMAs of another product:
+    //   slices 0-1 the in-lane max (masked keys excluded), slice 2 the lane-pair
+    //   max, the running max and the rescale factor, slices 3.. the 16
+    //   exponentials, their bf16 pairs (the MFMA operand) and the row sum.
+    // The running max is raised only when the half's max exceeds it by more
+    // than kMaxSlack, so the rescale is rare.
+    struct HalfSoftmax {
+        float mx, alpha;
+        float p[16];
+    };
+    constexpr int NSL = 8;
+    auto sm_slice = [&](auto MASKC, HalfSoftmax& st, f32x16& sh, bf16x8 (&pb)[2], int kh, int i)
+        __attribute__((always_inline)) {
         constexpr bool MASK = decltype(MASKC)::value;
-        const int k0 = kt * kFwdBN;
-        f32x16 s[2];
-        {
-            fetch(kn, nk, nv);
-            bf16x8 kf[2][KS];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = frag_at<HD>(sk, 32 * mt, off.frag[ks]);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) mfma_kq(s[mt], kf[mt][ks], qf[ks], ks == 0);
-        }
-        mfma_result_wait(s[0]);
-        mfma_result_wait(s[1]);
-        // softmax over the tile's 64 keys; register r of s[mt] holds key
-        // k0 + 32 mt + 8 (r >> 2) + 4 hf + (r & 3)
-        const int lk = lim - k0 - 4 * hf;
-        if constexpr (MASK) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+        const int lk = lim - kh - 4 * hf;  // register r is hidden iff 8 (r >> 2) + (r & 3) > lk
+        if (i == 0) {
+            if constexpr (MASK) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (32 * mt + 8 * (r >> 2) + (r & 3) > lk) s[mt][r] = -__builtin_inf();
-        }
-        float mx = __builtin_fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-        for (int j = 2; j < 32; j += 2)
-            mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[j >> 4][j & 15]), s[j >> 4][(j & 15) + 1]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                         false, false);
-        const float m = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cl2;
-        const float m_new = m > m_use + kMaxSlack ? m : m_use;
-        const float alpha = m_new == m_use ? 1.f : fast_exp2(m_use - m_new);
-        m_use = m_new;
-        l_run *= alpha;
-        bf16x8 pb[4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float p2[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = 2 * j + e;
-                    float x = fast_exp2(__builtin_fmaf(s[mt][r], cl2, -m_new));
-                    if constexpr (MASK)
-                        if (32 * mt + 8 * (r >> 2) + (r & 3) > lk) x = 0.f;
-                    p2[e] = x;
-                }
-                pb[2 * mt + (j >> 2)][2 * (j & 3)] = to_bf16(p2[0]);
-                pb[2 * mt + (j >> 2)][2 * (j & 3) + 1] = to_bf16(p2[1]);
-                l_run += p2[0] + p2[1];
-                // keep the sum here: the compiler would otherwise sink the chain
-                // (and every P it reads) to the end of the loop body
-                asm volatile("" : "+v"(l_run));
+                    if (8 * (r >> 2) + (r & 3) > lk) sh[r] = -__builtin_inf();
             }
+            st.mx = __builtin_fmaxf(sh[0], sh[1]);
+#pragma unroll
+            for (int r = 2; r < 8; r += 2)
+                st.mx = __builtin_fmaxf(__builtin_fmaxf(st.mx, sh[r]), sh[r + 1]);
+        } else if (i == 1) {
+#pragma unroll
+            for (int r = 8; r < 16; r += 2)
+                st.mx = __builtin_fmaxf(__builtin_fmaxf(st.mx, sh[r]), sh[r + 1]);
+        } else if (i == 2) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.mx),
+                                                             __float_as_uint(st.mx), false, false);
+            const float m =
+                __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * cl2;
+            const float m_new = m > m_use + kMaxSlack ? m : m_use;
+            st.alpha = m_new == m_use ? 1.f : fast_exp2(m_use - m_new);
+            m_use = m_new;
+            l_run *= st.alpha;
+        } else {
+            // elements [e0, e1) of the 16, in pairs
+            const int e0 = (i - 3) * 16 / (NSL - 3) & ~1, e1 = (i - 2) * 16 / (NSL - 3) & ~1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                if (e < e0 || e >= (i == NSL - 1 ? 16 : e1)) continue;
+                float x = fast_exp2(__builtin_fmaf(sh[e], cl2, -m_use));
+                if constexpr (MASK)
+                    if (8 * (e >> 2) + (e & 3) > lk) x = 0.f;
+                st.p[e] = x;
+                if (e & 1) {
+                    pb[e >> 3][(e & 7) - 1] = to_bf16(st.p[e - 1]);
+                    pb[e >> 3][e & 7] = to_bf16(x);
+                    l_run += st.p[e - 1] + x;
+                    // keep the sum here: the compiler would otherwise sink the
+                    // chain (and every P it reads) to the end of the loop body
+                    asm volatile("" : "+v"(l_run));
+                }
+            }
+        }
+    };
+    auto rescale = [&](float alpha) __attribute__((always_inline)) {
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
             // the factor passes through the asm so that the products cannot be
             // hoisted out of the branch (they are the identity when no lane needs them)
@@ -210,33 +209,79 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= a;
         }
-        // O^T += V^T P^T over the tile's four 16-key steps
-        {
-            bf16x8 vf[4][DT];
+    };
+
+    // One 64-key tile as two 32-key halves A and B: issue the next tile's loads
+    // into the other buffer (past the end: the last tile again), then
+    //   S_A | S_B with the softmax of A | PV_A with the softmax of B | PV_B,
+    // each "|" a scheduling barrier and each "with" a hand interleave of one
+    // MFMA and one slice of softmax work.  MASK: some keys of the tile are
+    // hidden from some rows of the wave.
+    auto tile = [&](auto MASKC, int kt, const bf16* sk, const bf16* sv, int kn, bf16* nk,
+                    bf16* nv) __attribute__((always_inline)) {
+        const int k0 = kt * kFwdBN;
+        f32x16 sA, sB;
+        bf16x8 pA[2], pB[2];
+        HalfSoftmax stA, stB;
+        bf16x8 kf[2][KS];
+        fetch(kn, nk, nv);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vf[ks][dt] = tr_at<HD>(sv, 16 * ks, off.tr[dt]);
+            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = frag_at<HD>(sk, 32 * mt, off.frag[ks]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < KS; ++ks) mfma_kq(sA, kf[0][ks], qf[ks], ks == 0);
+        mfma_result_wait(sA);
+        __builtin_amdgcn_sched_barrier(0);
+        // S_B with the softmax of A; the V_A fragments are read meanwhile
+        bf16x8 vA[2][DT], vB[2][DT];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vf[ks][dt], pb[ks], acc[dt]);
-            pipeline_schedule<8 * DT, 4 * DT, 2, 8>();
+        for (int i = 0; i < KS; ++i) {
+            mfma_kq(sB, kf[1][i], qf[i], i == 0);
+            sm_slice(MASKC, stA, sA, pA, k0, i * NSL / KS);
+            if (i * NSL / KS != (i + 1) * NSL / KS - 1)
+                for (int j = i * NSL / KS + 1; j < (i + 1) * NSL / KS; ++j)
+                    sm_slice(MASKC, stA, sA, pA, k0, j);
+            if (i >= KS - 2) {
+                const int kk = i - (KS - 2);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) vA[kk][dt] = tr_at<HD>(sv, 16 * kk, off.tr[dt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        mfma_result_wait(sB);
+        rescale(stA.alpha);
+        __builtin_amdgcn_sched_barrier(0);
+        // PV_A with the softmax of B; the V_B fragments are read meanwhile
+#pragma unroll
+        for (int i = 0; i < 2 * DT; ++i) {
+            const int kk = i / DT, dt = i % DT;
+            acc[dt] = mfma32(vA[kk][dt], pA[kk], acc[dt]);
+            sm_slice(MASKC, stB, sB, pB, k0 + 32, i * NSL / (2 * DT));
+            if (i * NSL / (2 * DT) != (i + 1) * NSL / (2 * DT) - 1)
+                for (int j = i * NSL / (2 * DT) + 1; j < (i + 1) * NSL / (2 * DT); ++j)
+                    sm_slice(MASKC, stB, sB, pB, k0 + 32, j);
+            if (i >= 2 * DT - 2) {
+                const int kb = i - (2 * DT - 2);
+#pragma unroll
+                for (int dt2 = 0; dt2 < DT; ++dt2)
+                    vB[kb][dt2] = tr_at<HD>(sv, 32 + 16 * kb, off.tr[dt2]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rescale(stB.alpha);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(vB[kk][dt], pB[kk], acc[dt]);
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto sync = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
-    // a tile of the causal tail: masked, plain or hidden for this wave
-    auto tail_tile = [&](int kt, const bf16* sk, const bf16* sv, int kn, bf16* nk, bf16* nv)
-        __attribute__((always_inline)) {
-        const int k0 = kt * kFwdBN;
-        if (k0 + kFwdBN - 1 <= qw0) tile(IntC<0>{}, kt, sk, sv, kn, nk, nv);
-        else if (k0 <= qw0 + 31) tile(IntC<1>{}, kt, sk, sv, kn, nk, nv);
-        else fetch(kn, nk, nv);  // no row of this wave sees these keys
-    };
-
     fetch(0, sK0, sV0);
     sync();
     int kt = 0;
@@ -246,11 +291,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
         tile(IntC<0>{}, kt + 1, sK1, sV1, min(kt + 2, nkt - 1), sK0, sV0);
         sync();
     }
-    for (; kt < nkt; ++kt) {
+    // the rest (the diagonal tiles of a causal walk among them) masked; a wave
+    // that sees none of a tile's keys only issues its share of the next loads.
+    // kt is even here, so the buffers alternate 0, 1 as in the loop above.
+    auto tail = [&](int kt, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv)
+        __attribute__((always_inline)) {
         const int kn = min(kt + 1, nkt - 1);
-        if (kt & 1) tail_tile(kt, sK1, sV1, kn, sK0, sV0);
-        else tail_tile(kt, sK0, sV0, kn, sK1, sV1);
+        if (kt * kFwdBN <= qw0 + 31) tile(IntC<1>{}, kt, sk, sv, kn, nk, nv);
+        else fetch(kn, nk, nv);
         sync();
+    };
+    for (; kt < nkt; kt += 2) {
+        tail(kt, sK0, sV0, sK1, sV1);
+        if (kt + 1 < nkt) tail(kt + 1, sK1, sV1, sK0, sV0);
     }
 
     // epilogue: O = O^T / l, LSE = (m + log2 l) ln 2 (l summed over the lane pair)
