@@ -25,6 +25,11 @@ gyom.fr, "LazyFlash allège la rétropropagation de l'attention, 5,72 fois"):
   gradient is unbiased in expectation (same section).
 * Sparse backward: skipped blocks contribute nothing and are never touched;
   kept blocks contribute their dense terms times w_b.
+* Other selection rules, compared with the budget at equal backward time
+  (section "Le choix des blocs pèse plus que la quantité sautée"): a fixed
+  fraction of blocks chosen once for the whole run, where the budget adapts;
+  and top-k, which removes the same blocks at every step, where the budget's
+  draw changes from step to step.
 
 Readings where the pages are silent (all listed in the design notes):
 * tau is the unique root of the budget equation for 0 < delta < 1 (the
@@ -39,6 +44,12 @@ Readings where the pages are silent (all listed in the design notes):
 * A head whose masses are not all finite keeps every block with w = 1 and
   tau = NaN, so non-finite values propagate as in the dense backward.
 * Grouped-query attention: query head h reads key/value head h // (Hq / Hkv).
+* Fixed fraction f in (0, 1]: the budget's draw (p_b = min(1, m_b / tau),
+  w = 1/p) with tau set so that the expected number of kept blocks,
+  sum_b p_b, is c = f * n, n the number of positive-mass blocks.
+* Top-k with fraction f in (0, 1]: keep the k = ceil(f * n) positive-mass
+  blocks of largest mass (ties: lower block index first), weight 1, no draw;
+  tau reports the smallest kept mass.
 """
 import math
 
@@ -48,7 +59,11 @@ __all__ = [
     "attn_fwd", "attn_fwd_rows", "attn_bwd_dense", "attn_bwd_sparse",
     "halving_tree_sum", "block_masses", "budget_discarded", "solve_tau",
     "philox4x64_10", "block_uniform", "select",
+    "RULE_BUDGET", "RULE_FRACTION", "RULE_TOPK", "expected_kept", "solve_tau_fraction",
+    "topk_keep", "select_rule",
 ]
+
+RULE_BUDGET, RULE_FRACTION, RULE_TOPK = 0, 1, 2
 
 MASK64 = (1 << 64) - 1
 
@@ -313,6 +328,116 @@ def select(mass, delta, seed):
                 if u[b, h, i] < pi:
                     keep[b, h, i] = True
                     w[b, h, i] = np.float32(1.0 / pi)
+            idx = np.nonzero(keep[b, h])[0]
+            kept_idx[b, h, :idx.size] = idx
+            kept_count[b, h] = idx.size
+    return dict(tau=tau, p=p, u=u, keep=keep, w=w, kept_idx=kept_idx, kept_count=kept_count)
+
+
+# --------------------------------------------------------------------------
+# other selection rules (section "Le choix des blocs pèse plus que la
+# quantité sautée")
+# --------------------------------------------------------------------------
+def expected_kept(m, tau):
+    """g(tau) = sum_b min(1, m_b / tau) over the positive masses."""
+    m = np.asarray(m, dtype=np.float64)
+    pos = m[m > 0.0]
+    return float(np.sum(np.minimum(1.0, pos / tau)))
+
+
+def solve_tau_fraction(m, f):
+    """tau of one (batch, head) for a fixed expected kept fraction f in (0, 1].
+
+    With the positive masses sorted ascending, m_(1) <= ... <= m_(n), and tau in
+    [m_(k), m_(k+1)], the k smallest have p = m / tau and the others p = 1, so
+    g(tau) = (n - k) + A_k / tau with A_k the running sum of the k smallest.
+    g falls as tau grows; the first interval whose right end already has
+    g <= c = f n holds the root tau = A_k / (c - (n - k)).  Sums run
+    sequentially in ascending order, one rounding per operation.  c >= n
+    keeps every positive block (tau = smallest positive mass); no positive
+    mass gives +inf; a non-finite mass gives NaN.
+    """
+    if not (0.0 < f <= 1.0):
+        raise ValueError("fraction must be in (0, 1]")
+    m = np.asarray(m, dtype=np.float64)
+    if not np.all(np.isfinite(m)):
+        return math.nan
+    pos = np.sort(m[m > 0.0])
+    n = pos.shape[0]
+    if n == 0:
+        return math.inf
+    c = f * float(n)
+    if c >= float(n):
+        return float(pos[0])
+    a = 0.0
+    for k in range(n):               # k + 1 smallest masses below tau
+        a = a + float(pos[k])
+        hi = float(pos[k + 1]) if k + 1 < n else math.inf
+        sat = float(n - k - 1)       # blocks at p = 1
+        if sat + a / hi <= c:
+            return a / (c - sat)
+    raise AssertionError("unreachable for 0 < c < n")
+
+
+def topk_keep(m, f):
+    """Keep mask of top-k for one (batch, head): the k = ceil(f n) positive
+    masses of largest value, ties to the lower block index."""
+    if not (0.0 < f <= 1.0):
+        raise ValueError("fraction must be in (0, 1]")
+    m = np.asarray(m, dtype=np.float64)
+    keep = np.zeros(m.shape[0], dtype=bool)
+    pos = np.nonzero(m > 0.0)[0]
+    k = min(pos.size, math.ceil(f * float(pos.size)))
+    order = sorted(pos.tolist(), key=lambda i: (-float(m[i]), i))
+    keep[order[:k]] = True
+    return keep
+
+
+def select_rule(mass, rule, param, seed):
+    """Keep set and weights from masses [B,H,nqb] for one of the rules:
+    RULE_BUDGET (param = delta, as select), RULE_FRACTION (param = f, the
+    budget's draw with tau from solve_tau_fraction) or RULE_TOPK (param = f,
+    deterministic, weight 1).  Same fields as select."""
+    if rule == RULE_BUDGET:
+        return select(mass, param, seed)
+    if rule not in (RULE_FRACTION, RULE_TOPK):
+        raise ValueError("unknown rule")
+    if not (0.0 < param <= 1.0):
+        raise ValueError("fraction must be in (0, 1]")
+    mass = np.asarray(mass, dtype=np.float64)
+    B, H, nqb = mass.shape
+    tau = np.empty((B, H))
+    p = np.zeros((B, H, nqb))
+    u = np.zeros((B, H, nqb))
+    keep = np.zeros((B, H, nqb), dtype=bool)
+    w = np.zeros((B, H, nqb), dtype=np.float32)
+    kept_idx = np.full((B, H, nqb), -1, dtype=np.int32)
+    kept_count = np.zeros((B, H), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            mh = mass[b, h]
+            if not np.all(np.isfinite(mh)):          # non-finite head: dense
+                tau[b, h] = math.nan
+                p[b, h] = 1.0
+                keep[b, h] = True
+                w[b, h] = 1.0
+            elif rule == RULE_TOPK:
+                kk = topk_keep(mh, param)
+                keep[b, h] = kk
+                p[b, h] = kk.astype(np.float64)
+                w[b, h] = np.where(kk, np.float32(1.0), np.float32(0.0))
+                tau[b, h] = float(mh[kk].min()) if kk.any() else math.inf
+            else:
+                t = solve_tau_fraction(mh, param)
+                tau[b, h] = t
+                for i in range(nqb):
+                    u[b, h, i] = block_uniform(seed, b, h, i)
+                    mi = float(mh[i])
+                    pi = 0.0 if mi == 0.0 else min(1.0, mi / t)
+                    p[b, h, i] = pi
+                    if u[b, h, i] < pi:
+                        keep[b, h, i] = True
+                        w[b, h, i] = np.float32(1.0 / pi)
             idx = np.nonzero(keep[b, h])[0]
             kept_idx[b, h, :idx.size] = idx
             kept_count[b, h] = idx.size
