@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--delta", type=float, default=None, help="main delta (default 0.1)")
     ap.add_argument("--sweep-steps", type=int, default=5,
                     help="steps per extra delta of the sweep (0: no sweep)")
+    ap.add_argument("--rule-steps", type=int, default=5,
+                    help="steps per selection rule of the equal-kept-fraction comparison (0: skip)")
     ap.add_argument("--train-steps", type=int, default=5,
                     help="timed steps of the autograd training step per delta (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,6 +221,11 @@ def main():
     others["select_mass_pass"]["achieved_incl_tau"] = round(
         others["select_mass_pass"]["bytes_per_launch"] / (t_sel * 1e-3) / 1e9, 1)
 
+    rules = None
+    if args.rule_steps > 0:
+        rules = selection_rules_report(cfg, q, k, v, o, lse, do, ws, main_delta,
+                                       float(kept.mean()), args.rule_steps)
+
     training = None
     if args.train_steps > 0:
         training = training_step_report(cfg, q, k, v, do, main_delta, args.train_steps)
@@ -262,6 +269,7 @@ def main():
             round((t_fwd + dense_ms) / (t_fwd + t_attn_bwd), 3) if dense_ms else None),
         "delta_sweep": sweep_out,
         "training_step": training,
+        "selection_rules": rules,
         "roofline": roofline,
         "bwd_walks": bwd_walks,
         "other_kernels": others,
@@ -272,6 +280,62 @@ def main():
                   "wall time of both loops per step",
     }
     print(json.dumps(out), flush=True)
+
+
+def selection_rules_report(cfg, q, k, v, o, lse, do, ws, delta, kept_frac, steps):
+    """The budget against a fixed fraction and top-k at the same kept fraction,
+    i.e. at equal backward work (LazyFlash entry, section on block choice).
+    Per rule: select + backward time, kept fraction, and the gradient's
+    distance to the dense gradient (delta = 0), relative, over dQ, dK, dV:
+    per step (the estimator's spread), and of the mean over the steps' draws
+    (what stays is bias: a random unbiased draw averages out, top-k drops the
+    same blocks every step)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_backward_amd import binding as bd
+
+    stream = torch.cuda.current_stream()
+    common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, workspace=ws)
+
+    def grads(rule, param, seed):
+        sel = bd.block_select(o, do, param, seed, block=cfg.block, causal=cfg.causal,
+                              scale=cfg.scale, heads_kv=cfg.Hkv, rule=rule)
+        return sel, bd.attn_bwd(q, k, v, lse, do, sel, **common)
+
+    _, dense = grads(bd.SELECT_BUDGET, 0.0, 0)
+    dense = [x.float() for x in dense]
+    dnorm = float(sum((x * x).sum() for x in dense).sqrt())
+    out = []
+    for name, rule, param in (("budget", bd.SELECT_BUDGET, delta),
+                              ("fixed_fraction", bd.SELECT_FRACTION, kept_frac),
+                              ("topk", bd.SELECT_TOPK, kept_frac)):
+        log(f"[bench] selection rule {name} ({param:.4g})")
+        grads(rule, param, 777)  # warm-up
+        ms, errs, kept = [], [], []
+        acc = [torch.zeros_like(x) for x in dense]
+        for s in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sel, g = grads(rule, param, s)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+            kept.append(float((sel["block_w"] != 0).float().mean().item()))
+            gf = [x.float() for x in g]
+            errs.append(float(sum(((a - b) ** 2).sum() for a, b in zip(gf, dense)).sqrt()) / dnorm)
+            for a, b in zip(acc, gf):
+                a += b
+        mean_err = float(sum(((a / steps - b) ** 2).sum() for a, b in zip(acc, dense)).sqrt()) / dnorm
+        out.append(dict(rule=name, param=round(float(param), 6), steps=steps,
+                        attn_bwd_ms=round(float(np.mean(ms)), 4),
+                        kept_fraction=round(float(np.mean(kept)), 5),
+                        grad_rel_err_per_step=round(float(np.mean(errs)), 5),
+                        grad_rel_err_of_mean=round(mean_err, 5)))
+    return {"workload": cfg.name, "note": "equal kept fraction = the budget's mean kept "
+            "fraction; errors relative to the dense gradient (delta = 0) over dQ, dK, dV; "
+            "attn_bwd_ms = select + backward, events around each step (no other work between)",
+            "rules": out}
 
 
 def training_step_report(cfg, q, k, v, do, delta, steps):

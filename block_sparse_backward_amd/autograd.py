@@ -43,33 +43,45 @@ class LazyFlashAttention(torch.autograd.Function):
     gradient mass (0 keeps every block: the exact dense gradient); seed keys
     the draw.  If `stats` is a dict, the backward stores in it the selection's
     device tensors (mass, tau, block_w, kept_idx, kept_count) without waiting
-    for them."""
+    for them.  `rule` (binding.SELECT_*) swaps the budget for a fixed-fraction
+    or top-k selection, delta then being the kept fraction."""
 
     @staticmethod
-    def forward(ctx, q, k, v, delta, seed, causal, scale, block, stats):
+    def forward(ctx, q, k, v, delta, seed, causal, scale, block, stats, rule=binding.SELECT_BUDGET):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         o, lse = binding.attn_fwd(q, k, v, causal=causal, scale=scale, block=block)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (float(delta), int(seed), bool(causal), scale, int(block), stats)
+        ctx.cfg = (float(delta), int(seed), bool(causal), scale, int(block), stats, int(rule))
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        delta, seed, causal, scale, block, stats = ctx.cfg
+        delta, seed, causal, scale, block, stats, rule = ctx.cfg
         do = do.to(q.dtype).contiguous()
         sel = binding.block_select(o, do, delta, seed, block=block, causal=causal, scale=scale,
-                                   heads_kv=k.shape[1])
+                                   heads_kv=k.shape[1], rule=rule)
         dq, dk, dv = binding.attn_bwd(q, k, v, lse, do, sel, block=block, causal=causal,
                                       scale=scale)
         if stats is not None:
             stats.update({n: sel[n] for n in ("mass", "tau", "block_w", "kept_idx",
                                               "kept_count")})
-        return dq, dk, dv, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
-def lazyflash_attention(q, k, v, delta, seed, causal=True, scale=None, block=128, stats=None):
-    """Functional form of LazyFlashAttention (scale defaults to 1/sqrt(d))."""
-    if not 0.0 <= float(delta) < 1.0:
-        raise ValueError(f"delta must lie in [0, 1), got {delta}")
-    return LazyFlashAttention.apply(q, k, v, delta, seed, causal, scale, block, stats)
+def lazyflash_attention(q, k, v, delta, seed, causal=True, scale=None, block=128, stats=None,
+                        rule=binding.SELECT_BUDGET):
+    """Functional form of LazyFlashAttention (scale defaults to 1/sqrt(d)).
+    `rule` selects the blocks by the budget (default; `delta` is the budget)
+    or, for comparisons, by a fixed fraction or top-k (`delta` is then the
+    kept fraction in (0, 1])."""
+    d = float(delta)
+    if rule == binding.SELECT_BUDGET:
+        if not 0.0 <= d < 1.0:
+            raise ValueError(f"delta must lie in [0, 1), got {delta}")
+    elif rule in (binding.SELECT_FRACTION, binding.SELECT_TOPK):
+        if not 0.0 < d <= 1.0:
+            raise ValueError(f"the kept fraction must lie in (0, 1], got {delta}")
+    else:
+        raise ValueError(f"unknown selection rule {rule}")
+    return LazyFlashAttention.apply(q, k, v, delta, seed, causal, scale, block, stats, rule)

@@ -16,12 +16,14 @@ __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block
            "EXPORTED_SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
-EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_attn_bwd", "lf_bwd_workspace_size",
+EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_block_select_rule", "lf_attn_bwd",
+                    "lf_bwd_workspace_size",
                     "lf_attn_bwd_phases", "lf_status_str", "lf_last_error", "lf_abi_version")
 BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 3
+SELECT_BUDGET, SELECT_FRACTION, SELECT_TOPK = 0, 1, 2
 
 
 class LazyFlashError(RuntimeError):
@@ -56,6 +58,8 @@ def load(path=LIB_PATH):
     lib.lf_attn_fwd.restype = I32
     lib.lf_block_select.argtypes = [S, P, P, D, U64, P, P, P, P, P, P, P]
     lib.lf_block_select.restype = I32
+    lib.lf_block_select_rule.argtypes = [S, P, P, I32, D, U64, P, P, P, P, P, P, P]
+    lib.lf_block_select_rule.restype = I32
     lib.lf_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.lf_attn_bwd.restype = I32
     lib.lf_bwd_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
@@ -154,11 +158,13 @@ def select_outputs(B, Hq, N, block, device):
 
 
 def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads_kv=None,
-                 out=None):
+                 out=None, rule=SELECT_BUDGET):
     """Masses, tau, draw and compaction.  Returns a dict of device tensors:
     D [B,Hq,N] f32, mass [B,Hq,nqb] f64, tau [B,Hq] f64, block_w [B,Hq,nqb] f32,
     kept_idx [B,Hq,nqb] i32, kept_count [B,Hq] i32 (`out`: preallocated dict
-    from select_outputs)."""
+    from select_outputs).  `rule` picks the selection rule (SELECT_BUDGET:
+    `delta` is the budget; SELECT_FRACTION or SELECT_TOPK: `delta` is the
+    kept fraction f in (0, 1])."""
     lib = load()
     B, Hq, N, d = o.shape
     shp = make_shape(B, Hq, heads_kv or Hq, N, d, block, causal,
@@ -175,10 +181,11 @@ def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads
     _need(out["block_w"], "block_w", (B, Hq, nqb), torch.float32, dev)
     _need(out["kept_idx"], "kept_idx", (B, Hq, nqb), torch.int32, dev)
     _need(out["kept_count"], "kept_count", (B, Hq), torch.int32, dev)
-    _check(lib, lib.lf_block_select(ctypes.byref(shp), _ptr(o), _ptr(dout), float(delta),
-                                    ctypes.c_uint64(int(seed) & (2**64 - 1)), _ptr(out["D"]),
-                                    _ptr(out["mass"]), _ptr(out["tau"]), _ptr(out["block_w"]),
-                                    _ptr(out["kept_idx"]), _ptr(out["kept_count"]), _stream(dev)))
+    _check(lib, lib.lf_block_select_rule(ctypes.byref(shp), _ptr(o), _ptr(dout), int(rule),
+                                         float(delta), ctypes.c_uint64(int(seed) & (2**64 - 1)),
+                                         _ptr(out["D"]), _ptr(out["mass"]), _ptr(out["tau"]),
+                                         _ptr(out["block_w"]), _ptr(out["kept_idx"]),
+                                         _ptr(out["kept_count"]), _stream(dev)))
     return out
 
 

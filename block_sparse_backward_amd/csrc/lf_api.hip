@@ -93,19 +93,33 @@ lf_status lf_attn_fwd(const lf_shape* s, const void* q, const void* k, const voi
     return hip_status(lf::launch_fwd(pb, q, k, v, o, lse, (hipStream_t)stream));
 }
 
-lf_status lf_block_select(const lf_shape* s, const void* o, const void* dout, double delta,
-                          uint64_t seed, float* D, double* mass, double* tau, float* block_w,
-                          int32_t* kept_idx, int32_t* kept_count, void* stream) {
+lf_status lf_block_select_rule(const lf_shape* s, const void* o, const void* dout,
+                               int32_t rule, double param, uint64_t seed, float* D, double* mass,
+                               double* tau, float* block_w, int32_t* kept_idx,
+                               int32_t* kept_count, void* stream) {
     lf::Problem pb;
     bool empty;
     lf_status st = check_shape(s, pb, empty);
     if (st != LF_OK) return st;
-    if (!(delta >= 0.0 && delta < 1.0)) return fail(LF_EINVAL, "delta must be in [0, 1)");
+    if (rule == LF_SELECT_BUDGET) {
+        if (!(param >= 0.0 && param < 1.0)) return fail(LF_EINVAL, "delta must be in [0, 1)");
+    } else if (rule == LF_SELECT_FRACTION || rule == LF_SELECT_TOPK) {
+        if (!(param > 0.0 && param <= 1.0)) return fail(LF_EINVAL, "fraction must be in (0, 1]");
+    } else {
+        return fail(LF_EINVAL, "unknown selection rule");
+    }
     if (empty) return hip_status(hipSuccess);
     if (any_null({o, dout, D, mass, tau, block_w, kept_idx, kept_count}))
         return fail(LF_EINVAL, "NULL tensor pointer");
-    return hip_status(lf::launch_select(pb, o, dout, delta, seed, D, mass, tau, block_w, kept_idx,
-                                        kept_count, (hipStream_t)stream));
+    return hip_status(lf::launch_select(pb, o, dout, rule, param, seed, D, mass, tau, block_w,
+                                        kept_idx, kept_count, (hipStream_t)stream));
+}
+
+lf_status lf_block_select(const lf_shape* s, const void* o, const void* dout, double delta,
+                          uint64_t seed, float* D, double* mass, double* tau, float* block_w,
+                          int32_t* kept_idx, int32_t* kept_count, void* stream) {
+    return lf_block_select_rule(s, o, dout, LF_SELECT_BUDGET, delta, seed, D, mass, tau, block_w,
+                                kept_idx, kept_count, stream);
 }
 
 lf_status lf_bwd_workspace_size(const lf_shape* s, size_t* bytes) {

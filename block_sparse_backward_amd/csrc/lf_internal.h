@@ -16,9 +16,10 @@ struct Problem {
 hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* v, void* o,
                       float* lse, hipStream_t st);
 
-hipError_t launch_select(const Problem& pb, const void* o, const void* dout, double delta,
-                         uint64_t seed, float* D, double* mass, double* tau, float* block_w,
-                         int32_t* kept_idx, int32_t* kept_count, hipStream_t st);
+// rule: 0 budget (param = delta), 1 fixed fraction, 2 top-k (param = f)
+hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int rule,
+                         double param, uint64_t seed, float* D, double* mass, double* tau,
+                         float* block_w, int32_t* kept_idx, int32_t* kept_count, hipStream_t st);
 
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,

@@ -128,25 +128,40 @@ __device__ __forceinline__ uint64_t philox_first_word(uint64_t c0, uint64_t c1, 
 // ---------------------------------------------------------------------------
 // Kernel B: one workgroup of 1024 threads per (b, h).
 // LDS: sorted masses, running sums A and Q (3 * P doubles, P = pow2 >= nqb).
+//
+// The rule that turns masses into a keep set (section "Le choix des blocs pèse
+// plus que la quantité sautée" compares the budget with two others):
+//   kRuleBudget   tau from the budget delta on the discarded mass (above);
+//   kRuleFraction the same draw with tau set so that the expected number of
+//                 kept blocks is f times the number of positive-mass blocks n:
+//                 on [m_(k), m_(k+1)] the expected count is (n - k) + A_k / tau,
+//                 so the first interval whose right end already gives <= f n
+//                 holds tau = A_k / (f n - (n - k));
+//   kRuleTopk     the ceil(f n) largest masses, ties to the lower index, weight
+//                 1, no draw; tau reports the smallest kept mass.
+// All floating-point steps are explicit roundings in a fixed order, so the
+// keep set is bit-reproducible.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
+constexpr int kRuleBudget = 0, kRuleFraction = 1, kRuleTopk = 2;
 
 __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
-    const double* __restrict__ mass, double delta, uint64_t seed, int Hq, int nqb, int P,
-    double* __restrict__ tau_out, float* __restrict__ block_w, int32_t* __restrict__ kept_idx,
-    int32_t* __restrict__ kept_count) {
+    const double* __restrict__ mass, int rule, double param, uint64_t seed, int Hq, int nqb,
+    int P, double* __restrict__ tau_out, float* __restrict__ block_w,
+    int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_count) {
     extern __shared__ double smem[];
     double* srt = smem;       // [P]
     double* accA = smem + P;  // [P]
     double* accQ = smem + 2 * P;
     __shared__ int s_nonfinite, s_npos, s_kstar, s_wave[kSelThreads / 64], s_base;
+    __shared__ int s_gt, s_eqw[kSelThreads / 64], s_eqbase;
     __shared__ double s_tau;
 
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
     const int b = bh / Hq, h = bh % Hq;
     const double* m = mass + (size_t)bh * nqb;
-    if (tid == 0) { s_nonfinite = 0; s_npos = 0; s_kstar = 0x7fffffff; s_base = 0; }
+    if (tid == 0) { s_nonfinite = 0; s_npos = 0; s_kstar = 0x7fffffff; s_base = 0; s_gt = 0; s_eqbase = 0; }
     __syncthreads();
 
     int my_pos = 0, my_bad = 0;
@@ -164,8 +179,15 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
     __syncthreads();
     const bool nonfinite = s_nonfinite != 0;
     const int n = s_npos;
+    // fraction and top-k: the target count f n (one rounding)
+    const double cnt = __dmul_rn(param, (double)n);
+    const bool need_sort = !nonfinite && n > 0 &&
+                           ((rule == kRuleBudget && param != 0.0) ||
+                            (rule == kRuleFraction && cnt < (double)n) || rule == kRuleTopk);
+    // top-k keeps the k largest: k = ceil(f n) (at least 1 for f > 0, n > 0)
+    const int topk = min(n, (int)ceil(cnt));
 
-    if (!nonfinite && n > 0 && delta != 0.0) {
+    if (need_sort) {
         // bitonic sort, ascending (positives first, +inf padding last)
         for (int k = 2; k <= P; k <<= 1) {
             for (int j = k >> 1; j > 0; j >>= 1) {
@@ -180,6 +202,10 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
                 __syncthreads();
             }
         }
+    }
+    if (need_sort && rule == kRuleTopk) {
+        if (tid == 0) s_tau = srt[n - topk];  // the k-th largest positive mass
+    } else if (need_sort) {
         // sequential running sums in ascending order (one rounding per op)
         if (tid == 0) {
             double a = 0.0, q = 0.0;
@@ -192,24 +218,38 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
             }
         }
         __syncthreads();
-        const double target = __dmul_rn(delta, accA[n - 1]);
-        // first interval [m_(k), m_(k+1)] whose right end meets the budget
-        for (int k = tid; k < n; k += kSelThreads) {
-            const double hi = (k + 1 < n) ? srt[k + 1] : __builtin_inf();
-            const double f_hi = __dsub_rn(accA[k], __ddiv_rn(accQ[k], hi));
-            if (f_hi >= target) atomicMin(&s_kstar, k);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            const int k = s_kstar;
-            s_tau = __ddiv_rn(accQ[k], __dsub_rn(accA[k], target));
+        if (rule == kRuleBudget) {
+            const double target = __dmul_rn(param, accA[n - 1]);
+            // first interval [m_(k), m_(k+1)] whose right end meets the budget
+            for (int k = tid; k < n; k += kSelThreads) {
+                const double hi = (k + 1 < n) ? srt[k + 1] : __builtin_inf();
+                const double f_hi = __dsub_rn(accA[k], __ddiv_rn(accQ[k], hi));
+                if (f_hi >= target) atomicMin(&s_kstar, k);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                const int k = s_kstar;
+                s_tau = __ddiv_rn(accQ[k], __dsub_rn(accA[k], target));
+            }
+        } else {
+            // first interval whose right end already brings the expected count to cnt
+            for (int k = tid; k < n; k += kSelThreads) {
+                const double hi = (k + 1 < n) ? srt[k + 1] : __builtin_inf();
+                const double sat = (double)(n - k - 1);
+                if (__dadd_rn(sat, __ddiv_rn(accA[k], hi)) <= cnt) atomicMin(&s_kstar, k);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                const int k = s_kstar;
+                s_tau = __ddiv_rn(accA[k], __dsub_rn(cnt, (double)(n - k - 1)));
+            }
         }
     } else if (tid == 0) {
         if (nonfinite) {
             s_tau = __builtin_nan("");
         } else if (n == 0) {
             s_tau = __builtin_inf();
-        } else {  // delta == 0: tau = smallest positive mass
+        } else {  // every positive block kept: tau = smallest positive mass
             double mn = __builtin_inf();
             for (int i = 0; i < nqb; ++i) {
                 const double mi = m[i];
@@ -220,25 +260,55 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
     }
     __syncthreads();
     const double tau = s_tau;
+    const bool topk_rule = rule == kRuleTopk && !nonfinite;
+    if (topk_rule && n > 0) {  // blocks strictly above the threshold are all kept
+        int my_gt = 0;
+        for (int i = tid; i < nqb; i += kSelThreads) my_gt += m[i] > tau;
+        if (my_gt) atomicAdd(&s_gt, my_gt);
+        __syncthreads();
+    }
+    const int ties_kept = topk_rule && n > 0 ? topk - s_gt : 0;  // of the blocks equal to tau
 
-    // draw, weights and ascending compaction, 1024 blocks per round
+    // draw (or top-k test), weights and ascending compaction, 1024 blocks per round
     const int lane = tid & 63, wave = tid >> 6;
     float* wout = block_w + (size_t)bh * nqb;
     int32_t* kout = kept_idx + (size_t)bh * nqb;
     for (int base = 0; base < nqb; base += kSelThreads) {
         const int i = base + tid;
-        bool keep = false;
+        bool keep = false, tie = false;
+        double p = 0.0;
         if (i < nqb) {
             const double mi = m[i];
-            double p;
-            if (nonfinite) p = 1.0;
-            else if (mi == 0.0) p = 0.0;
-            else p = fmin(1.0, __ddiv_rn(mi, tau));
-            const uint64_t x0 = philox_first_word((uint64_t)i, (uint64_t)h, (uint64_t)b, 0ull, seed, 0ull);
-            const double u = (double)(x0 >> 11) * 0x1p-53;
-            keep = u < p;
-            wout[i] = keep ? (float)__ddiv_rn(1.0, p) : 0.0f;
+            if (nonfinite) {
+                p = 1.0;
+            } else if (topk_rule) {
+                keep = n > 0 && mi > tau;
+                tie = n > 0 && mi == tau;
+            } else if (mi != 0.0) {
+                p = fmin(1.0, __ddiv_rn(mi, tau));
+            }
+            if (!topk_rule) {
+                const uint64_t x0 = philox_first_word((uint64_t)i, (uint64_t)h, (uint64_t)b, 0ull, seed, 0ull);
+                const double u = (double)(x0 >> 11) * 0x1p-53;
+                keep = u < p;
+            }
         }
+        if (topk_rule) {  // ties to the lower index: rank among this round's ties
+            const uint64_t tb = __ballot(tie);
+            const int trank = __popcll(tb & ((1ull << lane) - 1ull));
+            if (lane == 0) s_eqw[wave] = __popcll(tb);
+            __syncthreads();
+            int toff = s_eqbase;
+            for (int w = 0; w < wave; ++w) toff += s_eqw[w];
+            if (tie && toff + trank < ties_kept) keep = true;
+            __syncthreads();
+            if (tid == 0) {
+                int tot = 0;
+                for (int w = 0; w < kSelThreads / 64; ++w) tot += s_eqw[w];
+                s_eqbase += tot;
+            }
+        }
+        if (i < nqb) wout[i] = keep ? (topk_rule ? 1.0f : (float)__ddiv_rn(1.0, p)) : 0.0f;
         const uint64_t ballot = __ballot(keep);
         const int before = __popcll(ballot & ((1ull << lane) - 1ull));
         if (lane == 0) s_wave[wave] = __popcll(ballot);
@@ -284,9 +354,9 @@ static hipError_t launch_mass(const Problem& pb, const void* o, const void* dout
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_select(const Problem& pb, const void* o, const void* dout, double delta,
-                         uint64_t seed, float* D, double* mass, double* tau, float* block_w,
-                         int32_t* kept_idx, int32_t* kept_count, hipStream_t st) {
+hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int rule,
+                         double param, uint64_t seed, float* D, double* mass, double* tau,
+                         float* block_w, int32_t* kept_idx, int32_t* kept_count, hipStream_t st) {
     hipError_t e = pb.bf16 ? launch_mass<bf16>(pb, o, dout, D, mass, st)
                            : launch_mass<float>(pb, o, dout, D, mass, st);
     if (e != hipSuccess) return e;
@@ -299,7 +369,7 @@ hipError_t launch_select(const Problem& pb, const void* o, const void* dout, dou
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(tau_select_kernel, dim3((unsigned)(pb.B * pb.Hq)), dim3(kSelThreads), lds,
-                       st, mass, delta, seed, pb.Hq, pb.nqb, P, tau, block_w, kept_idx,
+                       st, mass, rule, param, seed, pb.Hq, pb.nqb, P, tau, block_w, kept_idx,
                        kept_count);
     return hipGetLastError();
 }

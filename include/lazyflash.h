@@ -115,6 +115,35 @@ lf_status lf_block_select(const lf_shape* shape, const void* o, const void* dout
                           void* stream);
 
 /*
+ * Block selection under another rule, for comparing rules at equal backward
+ * time (section "Le choix des blocs pèse plus que la quantité sautée" of the
+ * LazyFlash entry: the budget against a fixed fraction, chosen once where the
+ * budget adapts, and top-k, which drops the same blocks at every step where
+ * the budget's draw changes).  Same outputs, layouts and errors as
+ * lf_block_select; the backward consumes them unchanged.  With n the number
+ * of positive-mass blocks of a (batch, head):
+ *   LF_SELECT_BUDGET    param = delta in [0, 1): exactly lf_block_select;
+ *   LF_SELECT_FRACTION  param = f in (0, 1]: the budget's draw (Philox
+ *                       uniform, keep iff u < p, w = 1/p) with p = min(1, m/tau)
+ *                       and tau the root of sum_i p_i = f n, found on the
+ *                       sorted masses like the budget's tau (f n >= n keeps
+ *                       every positive block, tau = smallest positive mass);
+ *   LF_SELECT_TOPK      param = f in (0, 1]: the ceil(f n) largest masses, ties
+ *                       to the lower block index, weight 1, no draw (seed
+ *                       unused); tau = the smallest kept mass.
+ * Zero-mass blocks are never kept; a head with a non-finite mass keeps every
+ * block with weight 1 and tau = NaN under every rule.  An unknown rule or a
+ * parameter outside its range is LF_EINVAL.
+ */
+#define LF_SELECT_BUDGET 0
+#define LF_SELECT_FRACTION 1
+#define LF_SELECT_TOPK 2
+lf_status lf_block_select_rule(const lf_shape* shape, const void* o, const void* dout,
+                               int32_t rule, double param, uint64_t seed, float* D, double* mass,
+                               double* tau, float* block_w, int32_t* kept_idx,
+                               int32_t* kept_count, void* stream);
+
+/*
  * Block-sparse attention backward over the kept query blocks only.
  * Sections "Un budget sur la masse de gradient..." (skipped tiles are never
  * loaded nor computed) and "Trois tailles de modèle, 19 découpages sur 21"
@@ -181,7 +210,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 3
+#define LF_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

@@ -98,3 +98,25 @@ def test_new_seed_redraws_and_same_seed_repeats():
     for s, w in ((draw_seed(0), w1), (draw_seed(1), w3)):
         assert np.array_equal(w.cpu().numpy().view(np.uint32),
                               oracle.select(m, 0.3, s)["w"].view(np.uint32))
+
+
+@pytest.mark.parametrize("rule", ["fraction", "topk"])
+def test_autograd_with_other_selection_rules(rule):
+    from block_sparse_backward_amd import binding as bd
+    codes = {"fraction": (bd.SELECT_FRACTION, oracle.RULE_FRACTION),
+             "topk": (bd.SELECT_TOPK, oracle.RULE_TOPK)}[rule]
+    cfg = Config("ag7", 1, 4, 2, 512, 128, "bf16", True, 128, 2.0, boost_frac=0.25, boost=20.0)
+    inp = make_inputs(cfg, 0)
+    q, k, v = (_leaf(inp[n]) for n in ("q", "k", "v"))
+    stats = {}
+    o = lazyflash_attention(q, k, v, 0.4, 13, scale=cfg.scale, block=cfg.block, stats=stats,
+                            rule=codes[0])
+    o.backward(inp["dout"].to("cuda:0"))
+    torch.cuda.synchronize()
+    q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    ref = oracle.select_rule(oracle.block_masses(d64, cfg.block), codes[1], 0.4, 13)
+    assert np.array_equal(stats["block_w"].cpu().numpy().view(np.uint32), ref["w"].view(np.uint32))
+    g = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, ref["keep"], ref["w"], cfg.scale,
+                               True)
+    errs = [max_abs_rel(host(t.grad), r) for t, r in zip((q, k, v), g)]
+    assert max(errs) <= TOL["bf16"], errs
