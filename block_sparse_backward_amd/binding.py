@@ -146,7 +146,7 @@ def attn_fwd(q, k, v, causal=True, scale=None, block=128, out=None):
 
 def select_outputs(B, Hq, N, block, device):
     """Preallocated output tensors of block_select."""
-    nqb = N // block if block else 0
+    nqb = -(-N // block) if block else 0  # the last block may be partial
     return dict(
         D=torch.empty((B, Hq, N), dtype=torch.float32, device=device),
         mass=torch.empty((B, Hq, nqb), dtype=torch.float64, device=device),
@@ -172,7 +172,7 @@ def block_select(o, dout, delta, seed, block=128, causal=True, scale=None, heads
     dev = o.device
     _need(o, "o", o.shape, o.dtype, dev)
     _need(dout, "dout", o.shape, o.dtype, dev)
-    nqb = N // block if block else 0
+    nqb = -(-N // block) if block else 0  # the last block may be partial
     if out is None:
         out = select_outputs(B, Hq, N, block, dev)
     _need(out["D"], "D", (B, Hq, N), torch.float32, dev)
@@ -215,7 +215,7 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=No
     shp, _ = _shape_from(q, k, block, causal, scale)
     dev = q.device
     B, Hq, N, d = q.shape
-    nqb = N // block
+    nqb = -(-N // block)
     _need(k, "k", (B, shp.heads_kv, N, d), q.dtype, dev)
     _need(v, "v", k.shape, q.dtype, dev)
     _need(dout, "dout", q.shape, q.dtype, dev)

@@ -39,9 +39,8 @@ lf_status check_shape(const lf_shape* s, lf::Problem& pb, bool& empty) {
     if (!std::isfinite(s->scale)) return fail(LF_EINVAL, "scale must be finite");
     if (s->head_dim != 64 && s->head_dim != 128) return fail(LF_EUNSUPPORTED, "head_dim must be 64 or 128");
     if (s->block != 64 && s->block != 128) return fail(LF_EUNSUPPORTED, "block must be 64 or 128");
-    if (s->seqlen % s->block != 0)
-        return fail(LF_EUNSUPPORTED, "seqlen must be a multiple of block (variable-length batches are not implemented)");
-    if (s->seqlen / s->block > kMaxBlocksPerHead) return fail(LF_EUNSUPPORTED, "seqlen / block must be <= 4096");
+    if ((s->seqlen + s->block - 1) / s->block > kMaxBlocksPerHead)
+        return fail(LF_EUNSUPPORTED, "ceil(seqlen / block) must be <= 4096");
     const double elems = (double)s->batch * s->heads_q * s->seqlen * s->head_dim;
     if (elems > 9.0e15) return fail(LF_EINVAL, "tensor too large");
     pb.B = s->batch;
@@ -50,7 +49,7 @@ lf_status check_shape(const lf_shape* s, lf::Problem& pb, bool& empty) {
     pb.N = s->seqlen;
     pb.d = s->head_dim;
     pb.block = s->block;
-    pb.nqb = s->seqlen / s->block;
+    pb.nqb = (s->seqlen + s->block - 1) / s->block;  // the last block may be partial
     pb.causal = s->causal != 0;
     pb.scale = s->scale;
     pb.bf16 = s->dtype == LF_BF16;

@@ -236,6 +236,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     // A sub-tile's Q and dO rows go straight to LDS; LSE' and D take a
     // one-register path (they are transformed on the way).
     float pld = 0.f;
+    bool pld_ok = true;  // the staged row exists (the last block may be partial)
     const uint32_t head_bytes = (uint32_t)N * HD * sizeof(bf16);
     TileFetch<HD, kBM, 4> fq, fo;
     auto fetch = [&](int bh, int qs0, float lw, int BF) {
@@ -249,12 +250,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         // for this load, and with it for the tile loads issued just before.
         // Threads 0..63 load LSE, the others D (two waves load it twice): no
         // branch, so the loads can share a scheduling region with MFMAs.
-        pld = (tid < kBM ? lse : Drow)[(size_t)bh * N + qs0 + (tid & (kBM - 1))];
+        const int row = qs0 + (tid & (kBM - 1));
+        pld_ok = row < N;
+        pld = (tid < kBM ? lse : Drow)[(size_t)bh * N + (pld_ok ? row : N - 1)];
     };
-    // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and D
+    // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and D;
+    // rows past N get LSE' = +inf (P = 0) and D = 0, so they add nothing
     auto stage_rows = [&](int BF, float lw) {
-        if (tid < kBM) sLD[BF][0][tid] = pld * kLog2e - lw;
-        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld;
+        if (tid < kBM) sLD[BF][0][tid] = pld_ok ? pld * kLog2e - lw : __builtin_inf();
+        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld_ok ? pld : 0.f;
     };
     auto stage = [&](int BF, float lw) {
         fq.commit(sQD[BF][0], wave, lane);
@@ -548,7 +552,8 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
     const int tid = threadIdx.x;
     const int per = (E + 1023) / 1024;
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-    auto steps = [&](int i) { return causal ? (i * BLK + BLK - 1) / kQN + 1 : N / kQN; };
+    const int nks = (N + kQN - 1) / kQN;  // key steps of a head (the last may be partial)
+    auto steps = [&](int i) { return causal ? min((i * BLK + BLK - 1) / kQN + 1, nks) : nks; };
     auto entry = [&](int e, int& bh, int& i) {
         i = nqb - 1 - e / BHq;
         bh = e % BHq;
@@ -715,9 +720,11 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
             const int zn = __builtin_amdgcn_readfirstlane(item.z);
             for (int zz = 0; zz < zn; ++zz) {
                 const int blk = __builtin_amdgcn_readfirstlane(ws.skip[z0 + zz]);
-                u32x4* dst = reinterpret_cast<u32x4*>(dq + (size_t)blk * BLK * HD);
+                const int zbh = blk / nqb, zr0 = (blk % nqb) * BLK;
+                u32x4* dst = reinterpret_cast<u32x4*>(dq + ((size_t)zbh * N + zr0) * HD);
 #pragma unroll
-                for (int c = 0; c < BLK * HD / 8 / NT; ++c) dst[c * NT + tid] = u32x4{};
+                for (int c = 0; c < BLK * HD / 8 / NT; ++c)  // rows past N (a partial last block) stay untouched
+                    if (zr0 + (c * NT + tid) / (HD / 8) < N) dst[c * NT + tid] = u32x4{};
             }
             continue;
         }
@@ -730,16 +737,21 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
         const size_t qoff = (size_t)bh * N * HD;
         const float lw = __log2f(block_w[(size_t)bh * nqb + i]);
         const int qrow = i * BLK + 32 * wave + l32;  // query column held by this lane
+        // a row past N (the last block may be partial) reads row N - 1 and then
+        // gets zero fragments, LSE' = +inf (P = 0) and D = 0: it adds nothing
+        const bool row_ok = qrow < N;
+        const int qr = row_ok ? qrow : N - 1;
 
         // Q^T and dO^T fragments (B operands): column = query, k = head dim
         bf16x8 qf[KS], of[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
-            of[ks] = *reinterpret_cast<const bf16x8*>(dout + qoff + (size_t)qrow * HD + 16 * ks + 8 * hf);
+            qf[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + (size_t)qr * HD + 16 * ks + 8 * hf);
+            of[ks] = *reinterpret_cast<const bf16x8*>(dout + qoff + (size_t)qr * HD + 16 * ks + 8 * hf);
+            if (!row_ok) { qf[ks] = bf16x8{}; of[ks] = bf16x8{}; }
         }
-        const float lse_l = lse[(size_t)bh * N + qrow] * kLog2e - lw;
-        const float d_l = Drow[(size_t)bh * N + qrow];
+        const float lse_l = row_ok ? lse[(size_t)bh * N + qr] * kLog2e - lw : __builtin_inf();
+        const float d_l = row_ok ? Drow[(size_t)bh * N + qr] : 0.f;
 
         f32x16 acc[DT];
 #pragma unroll
@@ -884,7 +896,8 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
         __syncthreads();
         if (slot < 0) {
             bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
-            for (int c = tid; c < BLK * HD / 8; c += NT)
+            const int nrow = min(BLK, N - i * BLK);  // rows of the block that exist
+            for (int c = tid; c < nrow * HD / 8; c += NT)
                 reinterpret_cast<u32x4*>(dq_rows)[c] = reinterpret_cast<const u32x4*>(sA0)[c];
         } else {
             float* part = ws.part + (size_t)slot * BLK * HD;
@@ -902,16 +915,20 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
 // kDqFinSplit c + h does part h of the rows of chunked block c; the grid covers
 // the most chunked blocks the plan can list.
 template <int HD, int BLK>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(DqWorkspace ws, bf16* __restrict__ dq) {
+__global__ __launch_bounds__(256) void dq_finalize_kernel(DqWorkspace ws, bf16* __restrict__ dq,
+                                                          int N, int nqb) {
     const int c = blockIdx.x / kDqFinSplit, h = blockIdx.x % kDqFinSplit;
     if (c >= ws.ctrl[2]) return;
     const int e = ws.chunked[c];
     const int2 info = ws.blk[e];
     constexpr int NV = BLK * HD / 8 / kDqFinSplit;  // 8-element pieces of this workgroup
-    bf16x8* out = reinterpret_cast<bf16x8*>(dq + (size_t)e * BLK * HD) + h * NV;
+    const int r0 = (e % nqb) * BLK;
+    // pieces of rows past N (a partial last block) are not written
+    const int nv = min(NV, max(0, (min(BLK, N - r0) * HD / 8) - h * NV));
+    bf16x8* out = reinterpret_cast<bf16x8*>(dq + ((size_t)(e / nqb) * N + r0) * HD) + h * NV;
     const f32x4* p0 = reinterpret_cast<const f32x4*>(ws.part + (size_t)info.x * BLK * HD) + 2 * h * NV;
     constexpr size_t PS = (size_t)BLK * HD / 4;  // f32x4 per partial
-    for (int v = threadIdx.x; v < NV; v += 256) {
+    for (int v = threadIdx.x; v < nv; v += 256) {
         f32x4 s0 = p0[2 * v], s1 = p0[2 * v + 1];
         for (int j = 1; j < info.y; ++j) {
             s0 += p0[j * PS + 2 * v];
@@ -950,7 +967,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(
             const int i = kept_idx[(size_t)bh * nqb + pos];
             if ((unsigned)i >= (unsigned)nqb) continue;  // malformed list: skip
             const float w = block_w[(size_t)bh * nqb + i];
-            for (int r = i * blk; r < (i + 1) * blk; ++r) {
+            for (int r = i * blk; r < min((i + 1) * blk, N); ++r) {
                 if (causal && r < jrow) continue;
                 const float* qr = q + ((size_t)bh * N + r) * HD;
                 const float* dr = dout + ((size_t)bh * N + r) * HD;
@@ -1066,7 +1083,7 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
                                pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);                            \
             hipLaunchKernelGGL((dq_finalize_kernel<DD, BB>), dim3(kDqFinSplit * kDqChunkBelow),   \
                                dim3(256), 0, st,                                                \
-                               ws, (bf16*)dq);                                                  \
+                               ws, (bf16*)dq, pb.N, pb.nqb);                                    \
         }                                                                                       \
         return hipGetLastError();                                                               \
     }

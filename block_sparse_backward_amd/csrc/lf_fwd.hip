@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
     const int q0 = t * kFwdBM;
     const int qw0 = q0 + 32 * wave;  // first row of this wave
     const int qrow = qw0 + l32;      // query column held by this lane
-    const int lim = CAUSAL ? qrow : 0x7fffffff;  // keys past lim are hidden
+    const int lim = CAUSAL ? qrow : N - 1;  // keys past lim are hidden
 
     const size_t qoff = ((size_t)b * Hq + h) * (size_t)N * HD;
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
@@ -128,9 +128,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
     float m_use = -__builtin_inf(), l_run = 0.f;
 
     const int last_row = min(q0 + kFwdBM, N) - 1;
-    const int nkt = CAUSAL ? last_row / kFwdBN + 1 : N / kFwdBN;  // N is a multiple of 64
-    // tiles whose keys every row of the workgroup sees
-    const int nfull = CAUSAL ? min(q0 / kFwdBN, nkt) : nkt;
+    const int nkt = CAUSAL ? last_row / kFwdBN + 1 : (N + kFwdBN - 1) / kFwdBN;
+    // tiles whose keys every row of the workgroup sees (a partial last tile,
+    // past N, is masked)
+    const int nfull = CAUSAL ? min(q0 / kFwdBN, nkt) : N / kFwdBN;
     const TileOffsets<HD> off(lane);
 
     auto fetch = [&](int kt, bf16* dk, bf16* dv) __attribute__((always_inline)) {
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const bf16* __restrict
     auto tail = [&](int kt, const bf16* sk, const bf16* sv, bf16* nk, bf16* nv)
         __attribute__((always_inline)) {
         const int kn = min(kt + 1, nkt - 1);
-        if (kt * kFwdBN <= qw0 + 31) tile(IntC<1>{}, kt, sk, sv, kn, nk, nv);
+        if (!CAUSAL || kt * kFwdBN <= qw0 + 31) tile(IntC<1>{}, kt, sk, sv, kn, nk, nv);
         else fetch(kn, nk, nv);
         sync();
     };

@@ -20,7 +20,9 @@ namespace lf {
 
 // ---------------------------------------------------------------------------
 // Kernel A: one workgroup of 256 threads per query block (b, h, i).
-// The block is the contiguous run of L = block*d elements at offset blk*L.
+// The block is the run of L = block*d elements at row i*block of head (b, h);
+// when N is not a multiple of block the last block's missing rows read as
+// zeros (they add exact zeros to the mass) and get no D.
 // Thread t owns elements e + 8t + 2048s (e < 8, s < L/2048), loaded as one
 // 16-byte vector per s (coalesced), which lets the fp64 halving tree run as:
 // in-thread levels over s, then 8 cross-thread levels (t + 128, t + 64, ...,
@@ -30,24 +32,33 @@ template <typename T, int L, int HD>
 __global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
                                                      const T* __restrict__ dout,
                                                      float* __restrict__ D,
-                                                     double* __restrict__ mass) {
+                                                     double* __restrict__ mass, int N, int nqb) {
     constexpr int S = L / 2048;
     constexpr int LANES_PER_ROW = HD / 8;
+    constexpr int ROWS = L / HD;  // = block
     const size_t blk = blockIdx.x;
+    const size_t bh = blk / (size_t)nqb;
+    const int row0 = (int)(blk % (size_t)nqb) * ROWS;
+    const int nrows = min(ROWS, N - row0);  // rows of this block that exist
     const int t = threadIdx.x;
-    const T* g = dout + blk * (size_t)L;
-    const T* go = o + blk * (size_t)L;
+    const size_t base = (bh * (size_t)N + row0) * HD;
+    const T* g = dout + base;
+    const T* go = o + base;
 
     float x[S][8];
     float y[S][8];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        load8(g + 8 * t + 2048 * s, x[s]);
-        load8(go + 8 * t + 2048 * s, y[s]);
+        if ((8 * t + 2048 * s) / HD < nrows) {
+            load8(g + 8 * t + 2048 * s, x[s]);
+            load8(go + 8 * t + 2048 * s, y[s]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[s][e] = y[s][e] = 0.f;
+        }
     }
 
     // D: each (t, s) covers 8 columns of row (8t + 2048s) / HD.
-    constexpr int ROWS = L / HD;  // = block
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         float part = 0.f;
@@ -55,10 +66,8 @@ __global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
         for (int e = 0; e < 8; ++e) part += x[s][e] * y[s][e];
 #pragma unroll
         for (int off = LANES_PER_ROW / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        if ((t % LANES_PER_ROW) == 0) {
-            const int r = (8 * t + 2048 * s) / HD;
-            D[blk * (size_t)ROWS + r] = part;
-        }
+        const int r = (8 * t + 2048 * s) / HD;
+        if ((t % LANES_PER_ROW) == 0 && r < nrows) D[bh * (size_t)N + row0 + r] = part;
     }
 
     // Mass: squares are exact in fp64; only the additions round.
@@ -343,7 +352,7 @@ static hipError_t launch_mass(const Problem& pb, const void* o, const void* dout
 #define LF_MASS(LL, DD)                                                                     \
     if (L == LL && pb.d == DD) {                                                            \
         hipLaunchKernelGGL((mass_d_kernel<T, LL, DD>), dim3(nblk), dim3(256), 0, st, po, pd, \
-                           D, mass);                                                        \
+                           D, mass, pb.N, pb.nqb);                                          \
         return hipGetLastError();                                                           \
     }
     LF_MASS(4096, 64)

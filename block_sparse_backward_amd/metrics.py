@@ -32,10 +32,11 @@ def bwd_flops_kept(keep, N, d, block, causal):
     """keep: [..., nqb] boolean (or block weights, nonzero = kept)."""
     keep = np.asarray(keep) != 0
     idx = np.nonzero(keep)[-1].astype(np.int64)
+    rows = np.minimum(block, N - idx * block)  # the last block may be partial
     if causal:
-        pairs = block * (idx * block) + block * (block + 1) // 2
+        pairs = rows * (idx * block) + rows * (rows + 1) // 2
     else:
-        pairs = np.full(idx.shape, block * N, dtype=np.int64)
+        pairs = rows * N
     return int(10 * d * pairs.sum())
 
 

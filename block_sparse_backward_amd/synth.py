@@ -45,7 +45,7 @@ class Config:
 
     @property
     def nqb(self):
-        return self.N // self.block
+        return -(-self.N // self.block)  # the last block may be partial
 
     @property
     def scale(self):

@@ -47,8 +47,10 @@
  *   - An empty problem (batch == 0 or seqlen == 0) is valid and enqueues
  *     nothing; its tensor pointers may then be NULL.
  *   - Supported: dtype LF_BF16 or LF_F32, head_dim 64 or 128, block 64 or 128,
- *     seqlen a multiple of block, seqlen / block <= 4096, heads_q a multiple
- *     of heads_kv, finite scale.
+ *     ceil(seqlen / block) <= 4096, heads_q a multiple of heads_kv, finite
+ *     scale.  seqlen need not be a multiple of block: the last query block of
+ *     each head then has seqlen - (nqb - 1) * block rows (its mass sums those
+ *     rows; the backward treats it like any block).
  */
 #ifndef LAZYFLASH_H
 #define LAZYFLASH_H
@@ -107,7 +109,7 @@ lf_status lf_attn_fwd(const lf_shape* shape, const void* q, const void* k, const
  *   kept_idx [B,Hq,nqb] int32                          out: kept blocks ascending,
  *                                                           then -1 padding
  *   kept_count [B,Hq] int32                            out: number of kept blocks
- * nqb = seqlen / block.  Returns LF_EINVAL for delta outside [0, 1) or NaN.
+ * nqb = ceil(seqlen / block).  Returns LF_EINVAL for delta outside [0, 1) or NaN.
  */
 lf_status lf_block_select(const lf_shape* shape, const void* o, const void* dout,
                           double delta, uint64_t seed, float* D, double* mass, double* tau,

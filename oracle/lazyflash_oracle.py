@@ -175,7 +175,7 @@ def attn_bwd_sparse(q, k, v, dout, block, keep, w, scale, causal,
     for b, h in heads:
         g = h // G
         for i in np.nonzero(keep[b, h])[0]:
-            rows = np.arange(i * block, (i + 1) * block)
+            rows = np.arange(i * block, min((i + 1) * block, N))
             if o is None or lse is None:
                 o_rows, lse_rows = attn_fwd_rows(q[b, h], k[b, g], v[b, g], scale, causal, rows)
             else:
@@ -214,12 +214,16 @@ def block_masses(dout, block):
 
     dout [B,H,N,d] holds the exact values the kernel sees (bf16 or fp32
     upcast).  Their squares are exact in float64, so only the additions round,
-    in halving-tree order over the row-major flattening of the block.
+    in halving-tree order over the row-major flattening of the block.  When N
+    is not a multiple of block the last block has N - (nqb - 1) block rows; the
+    tree runs over the full block*d slots with the missing rows as zeros
+    (adding an exact zero changes nothing).
     """
     B, H, N, d = dout.shape
-    nqb = N // block
-    x = np.asarray(dout, dtype=np.float64).reshape(B, H, nqb, block * d)
-    return halving_tree_sum(x * x)
+    nqb = -(-N // block)
+    x = np.zeros((B, H, nqb * block, d))
+    x[:, :, :N] = np.asarray(dout, dtype=np.float64)
+    return halving_tree_sum((x * x).reshape(B, H, nqb, block * d))
 
 
 def budget_discarded(m, tau):

@@ -88,7 +88,7 @@ def _ws_size(lib, shp):
     (dict(scale=math.nan), bd.LF_EINVAL),
     (dict(head_dim=96), bd.LF_EUNSUPPORTED),
     (dict(block=32), bd.LF_EUNSUPPORTED),
-    (dict(seqlen=200), bd.LF_EUNSUPPORTED),
+    (dict(seqlen=128 * 4096 + 1), bd.LF_EUNSUPPORTED),   # 4097 blocks, the last partial
     (dict(seqlen=128 * 4097), bd.LF_EUNSUPPORTED),
 ])
 def test_bad_shapes_rejected_by_every_entry_point(kw, status):
@@ -192,3 +192,14 @@ def test_wrapper_and_binding_reject_host_tensors():
         lazyflash_attention(q, q, q, 1.0, 0, block=64)
     with pytest.raises(ValueError, match="delta"):
         lazyflash_attention(q, q, q, float("nan"), 0, block=64)
+
+
+def test_ragged_seqlen_passes_validation():
+    # N not a multiple of the block: the last query block is partial; the shape
+    # is valid, so only the NULL tensor pointers are reported
+    lib = bd.load()
+    shp = _shape(seqlen=200)
+    assert _fwd(lib, shp, ptr=NULL) == bd.LF_EINVAL
+    assert b"NULL" in lib.lf_last_error()
+    st, n = _ws_size(lib, shp)
+    assert st == bd.LF_OK and n > 0

@@ -30,6 +30,14 @@ SMALL = {
     "f32_noncausal_d128": (Config("s8", 1, 2, 1, 128, 128, "f32", False, 64, 1.0), 0.2),
     "bf16_boosted_heavy": (Config("s9", 1, 4, 2, 1024, 128, "bf16", True, 128, 2.0,
                                   boost_frac=0.1, boost=20.0), 0.1),
+    # N not a multiple of the block: a partial last query block and key tile
+    "bf16_ragged_N1000_b128": (Config("r1", 1, 4, 2, 1000, 128, "bf16", True, 128, 1.5), 0.1),
+    "bf16_ragged_N777_noncausal_d64": (Config("r2", 2, 2, 1, 777, 64, "bf16", False, 64, 1.0), 0.2),
+    "bf16_ragged_N1100_d64_b128_gqa4": (Config("r3", 1, 8, 2, 1100, 64, "bf16", True, 128, 2.0,
+                                               boost_frac=0.2, boost=20.0), 0.05),
+    "bf16_ragged_N333_noncausal_d128_b64": (Config("r4", 1, 2, 2, 333, 128, "bf16", False, 64, 0.5),
+                                            0.0),
+    "f32_ragged_N300": (Config("r5", 1, 2, 2, 300, 64, "f32", True, 64, 1.0), 0.1),
 }
 
 
@@ -53,7 +61,7 @@ def test_small_full_parity(name):
     print(f"[parity] {name} kept={ref_sel['keep'].mean():.3f} errs={errs}", flush=True)
     assert max(errs) <= tol, errs
     # rows of skipped blocks of dq are exact zeros
-    skipped = np.repeat(~ref_sel["keep"], cfg.block, axis=2)
+    skipped = np.repeat(~ref_sel["keep"], cfg.block, axis=2)[:, :, :cfg.N]
     assert np.all(host(gpu["dq"])[skipped] == 0.0)
 
 
@@ -89,6 +97,11 @@ MAXBLK = {
     "maxblk_1head_chunked": Config("maxblk1", 1, 1, 1, 4096 * 64, 64, "bf16", True, 64, 2.0,
                                    boost_frac=0.05, boost=20.0),
     "maxblk_gqa4": Config("maxblk4", 1, 4, 1, 4096 * 64, 64, "bf16", True, 64, 1.5),
+    # a long ragged length: 4096 blocks of 64 rows, the last with 27
+    "maxblk_ragged": Config("maxblkr", 1, 2, 1, 4095 * 64 + 27, 64, "bf16", True, 64, 2.0,
+                            boost_frac=0.05, boost=20.0),
+    "headline_ragged": Config("headr", 1, 8, 2, 32768 - 77, 128, "bf16", True, 128, 2.0,
+                              boost_frac=0.05, boost=20.0),
 }
 
 
@@ -160,7 +173,8 @@ def _check_large(cfg, inp, delta):
     # keys' dV sum to the weighted kept dO rows (per kv head, all query heads)
     dk_all = host(gpu["dk"]).sum(axis=2)
     dv_all = host(gpu["dv"]).sum(axis=2)
-    wrow = np.repeat(ref_sel["keep"] * ref_sel["w"].astype(np.float64), cfg.block, axis=2)
+    wrow = np.repeat(ref_sel["keep"] * ref_sel["w"].astype(np.float64), cfg.block,
+                     axis=2)[:, :, :cfg.N]
     want_dv = (d64 * wrow[..., None]).sum(axis=2).reshape(cfg.B, cfg.Hkv, G, cfg.d).sum(axis=2)
     scale_dk = np.abs(host(gpu["dk"])).max() * np.sqrt(cfg.N)
     assert np.abs(dk_all).max() <= 2e-2 * scale_dk
