@@ -13,14 +13,16 @@ import torch
 
 __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block_select",
            "select_outputs", "attn_bwd", "bwd_workspace_bytes", "bwd_workspace",
-           "EXPORTED_SYMBOLS", "LIB_PATH"]
+           "EXPORTED_SYMBOLS", "LIB_PATH", "attn_fwd_varlen", "block_select_varlen",
+           "attn_bwd_varlen", "varlen_block_offsets"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
 EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_block_select_rule", "lf_attn_bwd",
-                    "lf_bwd_workspace_size",
+                    "lf_bwd_workspace_size", "lf_attn_fwd_varlen", "lf_block_select_varlen",
+                    "lf_bwd_workspace_size_varlen", "lf_attn_bwd_varlen",
                     "lf_attn_bwd_phases", "lf_status_str", "lf_last_error", "lf_abi_version")
 BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 3
 SELECT_BUDGET, SELECT_FRACTION, SELECT_TOPK = 0, 1, 2
@@ -67,6 +69,15 @@ def load(path=LIB_PATH):
     lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z,
                                        ctypes.c_uint32, P]
     lib.lf_attn_bwd_phases.restype = I32
+    CU = ctypes.POINTER(ctypes.c_int32)
+    lib.lf_attn_fwd_varlen.argtypes = [S, CU, P, P, P, P, P, P]
+    lib.lf_attn_fwd_varlen.restype = I32
+    lib.lf_block_select_varlen.argtypes = [S, CU, P, P, I32, D, U64, P, P, P, P, P, P, P]
+    lib.lf_block_select_varlen.restype = I32
+    lib.lf_bwd_workspace_size_varlen.argtypes = [S, CU, ctypes.POINTER(ctypes.c_size_t)]
+    lib.lf_bwd_workspace_size_varlen.restype = I32
+    lib.lf_attn_bwd_varlen.argtypes = [S, CU, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.lf_attn_bwd_varlen.restype = I32
     lib.lf_status_str.argtypes = [I32]
     lib.lf_status_str.restype = ctypes.c_char_p
     lib.lf_last_error.argtypes = []
@@ -243,4 +254,94 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=No
         _check(lib, lib.lf_attn_bwd(*args, _stream(dev)))
     else:
         _check(lib, lib.lf_attn_bwd_phases(*args, ctypes.c_uint32(phases), _stream(dev)))
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# variable-length batches (layouts in include/lazyflash.h)
+# ---------------------------------------------------------------------------
+def _cu(cu_seqlens):
+    cu = [int(x) for x in cu_seqlens]
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    return cu, arr
+
+
+def varlen_block_offsets(cu_seqlens, block):
+    """cb[b] = blocks of the sequences before b (the packed block arrays)."""
+    cu = [int(x) for x in cu_seqlens]
+    cb = [0]
+    for b in range(len(cu) - 1):
+        cb.append(cb[-1] + -(-(cu[b + 1] - cu[b]) // block))
+    return cb
+
+
+def _varlen_shape(cu, Hq, Hkv, d, block, causal, scale, dtype):
+    return make_shape(len(cu) - 1, Hq, Hkv, 0, d, block, causal,
+                      d ** -0.5 if scale is None else scale, dtype)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, heads_q, heads_kv, head_dim, causal=True, scale=None,
+                    block=128):
+    """Forward over a variable-length batch; q, k, v are flat packed device
+    tensors.  Returns (o like q, lse float32 [Hq * total])."""
+    lib = load()
+    cu, arr = _cu(cu_seqlens)
+    shp = _varlen_shape(cu, heads_q, heads_kv, head_dim, block, causal, scale, q.dtype)
+    dev = q.device
+    o = torch.empty_like(q)
+    lse = torch.empty(heads_q * cu[-1], dtype=torch.float32, device=dev)
+    for t in (q, k, v):
+        _need(t, "tensor", t.shape, q.dtype, dev)
+    _check(lib, lib.lf_attn_fwd_varlen(ctypes.byref(shp), arr, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       _ptr(lse), _stream(dev)))
+    return o, lse
+
+
+def block_select_varlen(o, dout, cu_seqlens, heads_q, head_dim, delta, seed, block=128,
+                        causal=True, scale=None, heads_kv=None, rule=SELECT_BUDGET):
+    """Selection over a variable-length batch.  Returns a dict of flat device
+    tensors: D [Hq * total], mass / block_w / kept_idx [Hq * total_blocks],
+    tau / kept_count [Hq * B]."""
+    lib = load()
+    cu, arr = _cu(cu_seqlens)
+    cb = varlen_block_offsets(cu, block)
+    shp = _varlen_shape(cu, heads_q, heads_kv or heads_q, head_dim, block, causal, scale, o.dtype)
+    dev = o.device
+    B, nb = len(cu) - 1, cb[-1]
+    out = dict(
+        D=torch.empty(heads_q * cu[-1], dtype=torch.float32, device=dev),
+        mass=torch.empty(heads_q * nb, dtype=torch.float64, device=dev),
+        tau=torch.empty(heads_q * B, dtype=torch.float64, device=dev),
+        block_w=torch.empty(heads_q * nb, dtype=torch.float32, device=dev),
+        kept_idx=torch.empty(heads_q * nb, dtype=torch.int32, device=dev),
+        kept_count=torch.empty(heads_q * B, dtype=torch.int32, device=dev),
+    )
+    _need(o, "o", o.shape, o.dtype, dev)
+    _need(dout, "dout", o.shape, o.dtype, dev)
+    _check(lib, lib.lf_block_select_varlen(
+        ctypes.byref(shp), arr, _ptr(o), _ptr(dout), int(rule), float(delta),
+        ctypes.c_uint64(int(seed) & (2**64 - 1)), _ptr(out["D"]), _ptr(out["mass"]),
+        _ptr(out["tau"]), _ptr(out["block_w"]), _ptr(out["kept_idx"]), _ptr(out["kept_count"]),
+        _stream(dev)))
+    return out
+
+
+def attn_bwd_varlen(q, k, v, lse, dout, sel, cu_seqlens, heads_q, heads_kv, head_dim, block=128,
+                    causal=True, scale=None):
+    """Sparse backward over a variable-length batch (`sel` from
+    block_select_varlen).  Returns (dq, dk, dv) like q, k, v."""
+    lib = load()
+    cu, arr = _cu(cu_seqlens)
+    shp = _varlen_shape(cu, heads_q, heads_kv, head_dim, block, causal, scale, q.dtype)
+    dev = q.device
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.lf_bwd_workspace_size_varlen(ctypes.byref(shp), arr, ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for t in (q, k, v, dout):
+        _need(t, "tensor", t.shape, q.dtype, dev)
+    _check(lib, lib.lf_attn_bwd_varlen(
+        ctypes.byref(shp), arr, _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(sel["D"]),
+        _ptr(sel["kept_idx"]), _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
     return dq, dk, dv

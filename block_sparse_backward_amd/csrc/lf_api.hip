@@ -3,7 +3,9 @@
 // Validation touches no GPU state, so every error path runs without a device.
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "lazyflash.h"
 #include "lf_internal.h"
@@ -62,6 +64,44 @@ bool any_null(std::initializer_list<const void*> ptrs) {
         if (!p) return true;
     return false;
 }
+
+// A variable-length batch: shape->batch sequences, sequence b of
+// cu[b + 1] - cu[b] tokens (shape->seqlen is not used).  Checks every
+// sequence before anything is launched; fills one Problem per sequence.
+lf_status check_varlen(const lf_shape* s, const int32_t* cu, std::vector<lf::Problem>& seqs) {
+    if (!s) return fail(LF_EINVAL, "shape is NULL");
+    if (s->batch < 0) return fail(LF_EINVAL, "batch must be >= 0");
+    if (s->batch > 0 && !cu) return fail(LF_EINVAL, "cu_seqlens is NULL");
+    if (s->batch > 0 && cu[0] != 0) return fail(LF_EINVAL, "cu_seqlens[0] must be 0");
+    seqs.clear();
+    for (int b = 0; b < s->batch; ++b) {
+        if (cu[b + 1] < cu[b]) return fail(LF_EINVAL, "cu_seqlens must be nondecreasing");
+        lf_shape one = *s;
+        one.batch = 1;
+        one.seqlen = cu[b + 1] - cu[b];
+        lf::Problem pb;
+        bool empty;
+        const lf_status st = check_shape(&one, pb, empty);
+        if (st != LF_OK) return st;
+        pb.b0 = b;
+        seqs.push_back(pb);
+    }
+    if (s->batch == 0) {  // the shape's other fields are still checked
+        lf_shape one = *s;
+        one.batch = 0;
+        one.seqlen = 0;
+        lf::Problem pb;
+        bool empty;
+        return check_shape(&one, pb, empty);
+    }
+    return LF_OK;
+}
+
+// byte offset helpers for the packed layouts of a variable-length batch
+inline const void* at(const void* p, size_t bytes) { return static_cast<const char*>(p) + bytes; }
+inline void* at(void* p, size_t bytes) { return static_cast<char*>(p) + bytes; }
+template <typename T>
+inline T* at(T* p, size_t elems) { return p + elems; }
 
 }  // namespace
 
@@ -161,6 +201,114 @@ lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const voi
                       void* stream) {
     return lf_attn_bwd_phases(s, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv,
                               workspace, workspace_bytes, LF_BWD_ALL, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Variable-length batches (layouts in lazyflash.h): one launch sequence per
+// sequence on the caller's stream, each sequence a fixed-length problem of
+// batch 1 on its slice of the packed tensors.
+// ---------------------------------------------------------------------------
+lf_status lf_attn_fwd_varlen(const lf_shape* s, const int32_t* cu, const void* q, const void* k,
+                             const void* v, void* o, float* lse, void* stream) {
+    std::vector<lf::Problem> seqs;
+    lf_status st = check_varlen(s, cu, seqs);
+    if (st != LF_OK) return st;
+    if (cu && s->batch > 0 && cu[s->batch] > 0 && any_null({q, k, v, o, lse}))
+        return fail(LF_EINVAL, "NULL tensor pointer");
+    const size_t elt = s->dtype == LF_BF16 ? 2 : 4, d = (size_t)s->head_dim;
+    for (const lf::Problem& pb : seqs) {
+        if (pb.N == 0) continue;
+        const size_t t0 = (size_t)cu[pb.b0];
+        const hipError_t e = lf::launch_fwd(
+            pb, at(q, pb.Hq * t0 * d * elt), at(k, pb.Hkv * t0 * d * elt),
+            at(v, pb.Hkv * t0 * d * elt), at(o, pb.Hq * t0 * d * elt), at(lse, pb.Hq * t0),
+            (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(hipSuccess);
+}
+
+lf_status lf_block_select_varlen(const lf_shape* s, const int32_t* cu, const void* o,
+                                 const void* dout, int32_t rule, double param, uint64_t seed,
+                                 float* D, double* mass, double* tau, float* block_w,
+                                 int32_t* kept_idx, int32_t* kept_count, void* stream) {
+    std::vector<lf::Problem> seqs;
+    lf_status st = check_varlen(s, cu, seqs);
+    if (st != LF_OK) return st;
+    if (rule == LF_SELECT_BUDGET) {
+        if (!(param >= 0.0 && param < 1.0)) return fail(LF_EINVAL, "delta must be in [0, 1)");
+    } else if (rule == LF_SELECT_FRACTION || rule == LF_SELECT_TOPK) {
+        if (!(param > 0.0 && param <= 1.0)) return fail(LF_EINVAL, "fraction must be in (0, 1]");
+    } else {
+        return fail(LF_EINVAL, "unknown selection rule");
+    }
+    if (s->batch > 0 && any_null({o, dout, D, mass, tau, block_w, kept_idx, kept_count}))
+        return fail(LF_EINVAL, "NULL tensor pointer");
+    const size_t elt = s->dtype == LF_BF16 ? 2 : 4, d = (size_t)s->head_dim;
+    size_t cb = 0;  // blocks of the sequences before this one
+    for (const lf::Problem& pb : seqs) {
+        const size_t t0 = (size_t)cu[pb.b0], hq = (size_t)pb.Hq;
+        if (pb.N == 0) {  // no blocks: nothing kept, tau = +inf
+            const hipError_t e = lf::launch_empty_heads(at(tau, hq * pb.b0),
+                                                        at(kept_count, hq * pb.b0), pb.Hq,
+                                                        (hipStream_t)stream);
+            if (e != hipSuccess) return hip_status(e);
+            continue;
+        }
+        const hipError_t e = lf::launch_select(
+            pb, at(o, hq * t0 * d * elt), at(dout, hq * t0 * d * elt), rule, param, seed,
+            at(D, hq * t0), at(mass, hq * cb), at(tau, hq * pb.b0), at(block_w, hq * cb),
+            at(kept_idx, hq * cb), at(kept_count, hq * pb.b0), (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e);
+        cb += (size_t)pb.nqb;
+    }
+    return hip_status(hipSuccess);
+}
+
+lf_status lf_bwd_workspace_size_varlen(const lf_shape* s, const int32_t* cu, size_t* bytes) {
+    std::vector<lf::Problem> seqs;
+    lf_status st = check_varlen(s, cu, seqs);
+    if (st != LF_OK) return st;
+    if (!bytes) return fail(LF_EINVAL, "bytes is NULL");
+    size_t need = 0;
+    for (const lf::Problem& pb : seqs)
+        if (pb.N > 0) need = std::max(need, lf::bwd_workspace_bytes(pb));
+    *bytes = need;
+    return hip_status(hipSuccess);
+}
+
+lf_status lf_attn_bwd_varlen(const lf_shape* s, const int32_t* cu, const void* q, const void* k,
+                             const void* v, const float* lse, const void* dout, const float* D,
+                             const int32_t* kept_idx, const int32_t* kept_count,
+                             const float* block_w, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    std::vector<lf::Problem> seqs;
+    lf_status st = check_varlen(s, cu, seqs);
+    if (st != LF_OK) return st;
+    if (s->batch > 0 &&
+        any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv}))
+        return fail(LF_EINVAL, "NULL tensor pointer");
+    size_t need = 0;
+    for (const lf::Problem& pb : seqs)
+        if (pb.N > 0) need = std::max(need, lf::bwd_workspace_bytes(pb));
+    if (need > 0 && !workspace) return fail(LF_EINVAL, "workspace is NULL");
+    if (workspace_bytes < need) return fail(LF_EINVAL, "workspace too small (see lf_bwd_workspace_size_varlen)");
+    const size_t elt = s->dtype == LF_BF16 ? 2 : 4, d = (size_t)s->head_dim;
+    size_t cb = 0;
+    for (const lf::Problem& pb : seqs) {
+        if (pb.N == 0) continue;
+        const size_t t0 = (size_t)cu[pb.b0], hq = (size_t)pb.Hq, hk = (size_t)pb.Hkv;
+        // the sequences run one after the other on the stream and share the workspace
+        const hipError_t e = lf::launch_bwd(
+            pb, at(q, hq * t0 * d * elt), at(k, hk * t0 * d * elt), at(v, hk * t0 * d * elt),
+            at(lse, hq * t0), at(dout, hq * t0 * d * elt), at(D, hq * t0), at(kept_idx, hq * cb),
+            at(kept_count, hq * pb.b0), at(block_w, hq * cb), at(dq, hq * t0 * d * elt),
+            at(dk, hk * t0 * d * elt), at(dv, hk * t0 * d * elt), workspace, LF_BWD_ALL,
+            (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e);
+        cb += (size_t)pb.nqb;
+    }
+    return hip_status(hipSuccess);
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@ struct Problem {
     int B, Hq, Hkv, N, d, block, nqb, causal;
     float scale;
     bool bf16;
+    int b0 = 0;  // batch index of the first batch entry in the draw's counter
 };
 
 hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const void* v, void* o,
@@ -20,6 +21,9 @@ hipError_t launch_fwd(const Problem& pb, const void* q, const void* k, const voi
 hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int rule,
                          double param, uint64_t seed, float* D, double* mass, double* tau,
                          float* block_w, int32_t* kept_idx, int32_t* kept_count, hipStream_t st);
+
+// tau = +inf and kept_count = 0 for the n heads of an empty sequence
+hipError_t launch_empty_heads(double* tau, int32_t* kept_count, int n, hipStream_t st);
 
 hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const void* v,
                       const float* lse, const void* dout, const float* D,

@@ -155,8 +155,8 @@ constexpr int kSelThreads = 1024;
 constexpr int kRuleBudget = 0, kRuleFraction = 1, kRuleTopk = 2;
 
 __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
-    const double* __restrict__ mass, int rule, double param, uint64_t seed, int Hq, int nqb,
-    int P, double* __restrict__ tau_out, float* __restrict__ block_w,
+    const double* __restrict__ mass, int rule, double param, uint64_t seed, int b0, int Hq,
+    int nqb, int P, double* __restrict__ tau_out, float* __restrict__ block_w,
     int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_count) {
     extern __shared__ double smem[];
     double* srt = smem;       // [P]
@@ -297,7 +297,8 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
                 p = fmin(1.0, __ddiv_rn(mi, tau));
             }
             if (!topk_rule) {
-                const uint64_t x0 = philox_first_word((uint64_t)i, (uint64_t)h, (uint64_t)b, 0ull, seed, 0ull);
+                const uint64_t x0 = philox_first_word((uint64_t)i, (uint64_t)h, (uint64_t)(b0 + b), 0ull,
+                                                      seed, 0ull);
                 const double u = (double)(x0 >> 11) * 0x1p-53;
                 keep = u < p;
             }
@@ -363,6 +364,21 @@ static hipError_t launch_mass(const Problem& pb, const void* o, const void* dout
     return hipErrorInvalidValue;
 }
 
+__global__ void empty_heads_kernel(double* __restrict__ tau, int32_t* __restrict__ kept_count,
+                                   int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        tau[i] = __builtin_inf();
+        kept_count[i] = 0;
+    }
+}
+
+hipError_t launch_empty_heads(double* tau, int32_t* kept_count, int n, hipStream_t st) {
+    hipLaunchKernelGGL(empty_heads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       tau, kept_count, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int rule,
                          double param, uint64_t seed, float* D, double* mass, double* tau,
                          float* block_w, int32_t* kept_idx, int32_t* kept_count, hipStream_t st) {
@@ -378,8 +394,8 @@ hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(tau_select_kernel, dim3((unsigned)(pb.B * pb.Hq)), dim3(kSelThreads), lds,
-                       st, mass, rule, param, seed, pb.Hq, pb.nqb, P, tau, block_w, kept_idx,
-                       kept_count);
+                       st, mass, rule, param, seed, pb.b0, pb.Hq, pb.nqb, P, tau, block_w,
+                       kept_idx, kept_count);
     return hipGetLastError();
 }
 

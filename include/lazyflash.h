@@ -202,6 +202,44 @@ lf_status lf_attn_bwd_phases(const lf_shape* shape, const void* q, const void* k
                              const float* block_w, void* dq, void* dk, void* dv, void* workspace,
                              size_t workspace_bytes, uint32_t phases, void* stream);
 
+/*
+ * Variable-length batches (a batch of sequences of different lengths, packed
+ * without padding: the pages' workload is examples cut to each length, section
+ * "À 32 000 tokens, 5,72 fois sur l'attention arrière" of the LazyFlash entry).
+ * shape->batch is the number of sequences B; shape->seqlen is not used.
+ * cu_seqlens is a HOST array of B + 1 token offsets: cu[0] = 0, nondecreasing,
+ * sequence b has L_b = cu[b + 1] - cu[b] tokens (0 allowed).  Each sequence is
+ * one fixed-length problem of batch 1 and length L_b (all rules above apply
+ * per sequence, L_b need not be a multiple of block), stored as consecutive
+ * slices of the packed buffers:
+ *   q, o, dout, dq   [Hq, L_b, d] at element offset Hq * cu[b] * d
+ *   k, v, dk, dv     [Hkv, L_b, d] at element offset Hkv * cu[b] * d
+ *   lse, D           [Hq, L_b] at element offset Hq * cu[b]
+ *   mass, block_w, kept_idx   [Hq, nqb_b] at element offset Hq * cb[b],
+ *                    nqb_b = ceil(L_b / block), cb[b] = sum over j < b of nqb_j
+ *   tau, kept_count  [Hq] at element offset Hq * b
+ * The selection draw of block i of head h of sequence b is the draw of batch
+ * entry b (counter (i, h, b, 0)), so sequences never share uniforms.  Every
+ * sequence is checked before anything is enqueued; the work of the sequences
+ * is enqueued one after the other on `stream` (the backward's sequences share
+ * the workspace, which must hold lf_bwd_workspace_size_varlen bytes).  An
+ * empty sequence gets tau = +inf and kept_count = 0 and nothing else.
+ */
+lf_status lf_attn_fwd_varlen(const lf_shape* shape, const int32_t* cu_seqlens, const void* q,
+                             const void* k, const void* v, void* o, float* lse, void* stream);
+lf_status lf_block_select_varlen(const lf_shape* shape, const int32_t* cu_seqlens,
+                                 const void* o, const void* dout, int32_t rule, double param,
+                                 uint64_t seed, float* D, double* mass, double* tau,
+                                 float* block_w, int32_t* kept_idx, int32_t* kept_count,
+                                 void* stream);
+lf_status lf_bwd_workspace_size_varlen(const lf_shape* shape, const int32_t* cu_seqlens,
+                                       size_t* bytes);
+lf_status lf_attn_bwd_varlen(const lf_shape* shape, const int32_t* cu_seqlens, const void* q,
+                             const void* k, const void* v, const float* lse, const void* dout,
+                             const float* D, const int32_t* kept_idx, const int32_t* kept_count,
+                             const float* block_w, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* lf_status_str(lf_status status);
 
@@ -212,7 +250,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 4
+#define LF_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -297,12 +297,14 @@ def block_uniform(seed, b, h, i):
     return (x0 >> 11) * 2.0 ** -53
 
 
-def select(mass, delta, seed):
+def select(mass, delta, seed, b0=0):
     """Keep set and weights from masses [B,H,nqb] for budget delta and seed.
 
     Returns a dict with tau [B,H] float64, p, u [B,H,nqb] float64,
     keep [B,H,nqb] bool, w [B,H,nqb] float32 (0 when skipped),
     kept_idx [B,H,nqb] int32 (ascending, -1 padded), kept_count [B,H] int32.
+    b0 is the batch index of mass[0] in the draw's counter (sequence b0 + b of
+    a variable-length batch is drawn as batch entry b0 + b).
     """
     if not (0.0 <= delta < 1.0):
         raise ValueError("delta must be in [0, 1)")
@@ -320,7 +322,7 @@ def select(mass, delta, seed):
             t = solve_tau(mass[b, h], delta)
             tau[b, h] = t
             for i in range(nqb):
-                u[b, h, i] = block_uniform(seed, b, h, i)
+                u[b, h, i] = block_uniform(seed, b0 + b, h, i)
                 mi = float(mass[b, h, i])
                 if math.isnan(t):                       # non-finite head: dense
                     pi = 1.0
@@ -397,13 +399,13 @@ def topk_keep(m, f):
     return keep
 
 
-def select_rule(mass, rule, param, seed):
+def select_rule(mass, rule, param, seed, b0=0):
     """Keep set and weights from masses [B,H,nqb] for one of the rules:
     RULE_BUDGET (param = delta, as select), RULE_FRACTION (param = f, the
     budget's draw with tau from solve_tau_fraction) or RULE_TOPK (param = f,
-    deterministic, weight 1).  Same fields as select."""
+    deterministic, weight 1).  Same fields and b0 as select."""
     if rule == RULE_BUDGET:
-        return select(mass, param, seed)
+        return select(mass, param, seed, b0)
     if rule not in (RULE_FRACTION, RULE_TOPK):
         raise ValueError("unknown rule")
     if not (0.0 < param <= 1.0):
@@ -435,7 +437,7 @@ def select_rule(mass, rule, param, seed):
                 t = solve_tau_fraction(mh, param)
                 tau[b, h] = t
                 for i in range(nqb):
-                    u[b, h, i] = block_uniform(seed, b, h, i)
+                    u[b, h, i] = block_uniform(seed, b0 + b, h, i)
                     mi = float(mh[i])
                     pi = 0.0 if mi == 0.0 else min(1.0, mi / t)
                     p[b, h, i] = pi

@@ -203,3 +203,48 @@ def test_ragged_seqlen_passes_validation():
     assert b"NULL" in lib.lf_last_error()
     st, n = _ws_size(lib, shp)
     assert st == bd.LF_OK and n > 0
+
+
+def _varlen(lib, shp, cu, ptr=FAKE):
+    arr = (ctypes.c_int32 * len(cu))(*cu) if cu is not None else None
+    f = lib.lf_attn_fwd_varlen(ctypes.byref(shp), arr, ptr, ptr, ptr, ptr, ptr, NULL)
+    s = lib.lf_block_select_varlen(ctypes.byref(shp), arr, ptr, ptr, 0, 0.1, 0, ptr, ptr, ptr,
+                                   ptr, ptr, ptr, NULL)
+    b = lib.lf_attn_bwd_varlen(ctypes.byref(shp), arr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                               ptr, ptr, ptr, ptr, ptr, BIG, NULL)
+    n = ctypes.c_size_t(7)
+    w = lib.lf_bwd_workspace_size_varlen(ctypes.byref(shp), arr, ctypes.byref(n))
+    return f, s, b, w, n.value
+
+
+@pytest.mark.parametrize("cu,status", [
+    ([1, 5, 9], bd.LF_EINVAL),                 # must start at 0
+    ([0, 300, 200], bd.LF_EINVAL),             # decreasing
+    ([0, 300, 300 + 128 * 4096 + 1], bd.LF_EUNSUPPORTED),  # one sequence too long
+])
+def test_varlen_bad_offsets_rejected_before_any_launch(cu, status):
+    lib = bd.load()
+    shp = _shape(batch=len(cu) - 1, seqlen=0)
+    f, s, b, w, _ = _varlen(lib, shp, cu)
+    assert f == s == b == w == status
+
+
+def test_varlen_null_offsets_and_pointers():
+    lib = bd.load()
+    shp = _shape(batch=2, seqlen=0)
+    assert _varlen(lib, shp, None)[:4] == (bd.LF_EINVAL,) * 4
+    f, s, b, w, n = _varlen(lib, shp, [0, 100, 356], ptr=NULL)
+    assert (f, s, b) == (bd.LF_EINVAL,) * 3
+    assert w == bd.LF_OK
+    # the workspace of the longest sequence serves every sequence
+    one = _shape(batch=1, seqlen=256)
+    assert n == _ws_size(lib, one)[1] > 0
+
+
+def test_varlen_bad_rule_parameter():
+    lib = bd.load()
+    shp = _shape(batch=1, seqlen=0)
+    arr = (ctypes.c_int32 * 2)(0, 256)
+    for rule, param in ((0, 1.0), (1, 0.0), (2, 1.5), (9, 0.5)):
+        assert lib.lf_block_select_varlen(ctypes.byref(shp), arr, FAKE, FAKE, rule, param, 0,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == bd.LF_EINVAL
