@@ -242,6 +242,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     auto fetch = [&](int bh, int qs0, float lw, int BF) {
         (void)lw;
         (void)BF;
+        // the sub-tile is wave-uniform: keep its offsets scalar (a vector soffset
+        // would turn each buffer load into a loop over distinct values)
+        bh = __builtin_amdgcn_readfirstlane(bh);
+        qs0 = __builtin_amdgcn_readfirstlane(qs0);
         const size_t hoff = (size_t)bh * N * HD;
         const int soff = qs0 * HD * (int)sizeof(bf16);
         fq.issue(make_rsrc(q + hoff, head_bytes), soff, wave, lane);
@@ -722,9 +726,12 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
                 const int blk = __builtin_amdgcn_readfirstlane(ws.skip[z0 + zz]);
                 const int zbh = blk / nqb, zr0 = (blk % nqb) * BLK;
                 u32x4* dst = reinterpret_cast<u32x4*>(dq + ((size_t)zbh * N + zr0) * HD);
+                if (zr0 + BLK <= N) {
 #pragma unroll
-                for (int c = 0; c < BLK * HD / 8 / NT; ++c)  // rows past N (a partial last block) stay untouched
-                    if (zr0 + (c * NT + tid) / (HD / 8) < N) dst[c * NT + tid] = u32x4{};
+                    for (int c = 0; c < BLK * HD / 8 / NT; ++c) dst[c * NT + tid] = u32x4{};
+                } else {  // a partial last block: rows past N stay untouched
+                    for (int c = tid; c < (N - zr0) * HD / 8; c += NT) dst[c] = u32x4{};
+                }
             }
             continue;
         }
@@ -897,8 +904,15 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
         if (slot < 0) {
             bf16* dq_rows = dq + qoff + (size_t)i * BLK * HD;
             const int nrow = min(BLK, N - i * BLK);  // rows of the block that exist
-            for (int c = tid; c < nrow * HD / 8; c += NT)
-                reinterpret_cast<u32x4*>(dq_rows)[c] = reinterpret_cast<const u32x4*>(sA0)[c];
+            if (nrow == BLK) {
+#pragma unroll
+                for (int c = 0; c < BLK * HD / 8 / NT; ++c)
+                    reinterpret_cast<u32x4*>(dq_rows)[c * NT + tid] =
+                        reinterpret_cast<const u32x4*>(sA0)[c * NT + tid];
+            } else {
+                for (int c = tid; c < nrow * HD / 8; c += NT)
+                    reinterpret_cast<u32x4*>(dq_rows)[c] = reinterpret_cast<const u32x4*>(sA0)[c];
+            }
         } else {
             float* part = ws.part + (size_t)slot * BLK * HD;
             constexpr int PB = WPB * WREG / 4;  // 16-byte pieces per buffer

@@ -28,6 +28,29 @@ namespace lf {
 // in-thread levels over s, then 8 cross-thread levels (t + 128, t + 64, ...,
 // t + 1), then 3 in-vector levels over e.
 // ---------------------------------------------------------------------------
+// Eight consecutive elements as floats from a raw buffer (16-byte loads; past
+// the buffer's end they read as zeros).
+template <typename T>
+__device__ __forceinline__ void load8_buf(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
+                                          float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(r[j] << 16);
+            x[2 * j + 1] = __uint_as_float(r[j] & 0xffff0000u);
+        }
+    } else {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = __uint_as_float(a[j]);
+            x[4 + j] = __uint_as_float(b[j]);
+        }
+    }
+}
+
 template <typename T, int L, int HD>
 __global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
                                                      const T* __restrict__ dout,
@@ -41,21 +64,20 @@ __global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
     const int row0 = (int)(blk % (size_t)nqb) * ROWS;
     const int nrows = min(ROWS, N - row0);  // rows of this block that exist
     const int t = threadIdx.x;
-    const size_t base = (bh * (size_t)N + row0) * HD;
-    const T* g = dout + base;
-    const T* go = o + base;
+    // buffer loads over the head: rows past N read as zeros, with no branch
+    const size_t head = bh * (size_t)N * HD;
+    const uint32_t head_bytes = (uint32_t)((size_t)N * HD * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dout + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + head, head_bytes);
+    const int off0 = row0 * HD * (int)sizeof(T);  // the block's first row in the head
 
     float x[S][8];
     float y[S][8];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        if ((8 * t + 2048 * s) / HD < nrows) {
-            load8(g + 8 * t + 2048 * s, x[s]);
-            load8(go + 8 * t + 2048 * s, y[s]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[s][e] = y[s][e] = 0.f;
-        }
+        const int vo = (8 * t + 2048 * s) * (int)sizeof(T);
+        load8_buf<T>(rg, vo, off0, x[s]);
+        load8_buf<T>(ro, vo, off0, y[s]);
     }
 
     // D: each (t, s) covers 8 columns of row (8t + 2048s) / HD.
