@@ -42,6 +42,9 @@ def parse():
                     help="steps per selection rule of the equal-kept-fraction comparison (0: skip)")
     ap.add_argument("--train-steps", type=int, default=5,
                     help="timed steps of the autograd training step per delta (0: skip)")
+    ap.add_argument("--ceiling-reps", type=int, default=5,
+                    help="timed reps of the vendor bf16 GEMM that measures the practical MFMA "
+                         "ceiling of this GPU (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds spent on the oracle baseline sample")
@@ -230,6 +233,13 @@ def main():
     if args.train_steps > 0:
         training = training_step_report(cfg, q, k, v, do, main_delta, args.train_steps)
 
+    ceiling = None
+    if args.ceiling_reps > 0:
+        log("[bench] vendor GEMM ceiling")
+        ceiling = mfma_ceiling(args.ceiling_reps, peak)
+        ceiling["dkdv_vs_ceiling"] = round(achieved / ceiling["achieved"], 4)
+        ceiling["fwd_vs_ceiling"] = round(others["fwd"]["achieved"] / ceiling["achieved"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, main_delta, args.cpu_budget_s, metrics)
@@ -273,6 +283,7 @@ def main():
         "roofline": roofline,
         "bwd_walks": bwd_walks,
         "other_kernels": others,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         "timing": "HIP events on the launch stream, steady state (caches not flushed); the "
                   "steps' forwards run first, then their select+bwd back to back (a training "
@@ -280,6 +291,34 @@ def main():
                   "wall time of both loops per step",
     }
     print(json.dumps(out), flush=True)
+
+
+def mfma_ceiling(reps, peak, n=16384):
+    """The bf16 MFMA rate this GPU sustains on a plain large GEMM (the vendor
+    library behind torch.matmul, N(0,1) operands), timed like the kernels.
+    Sustained MFMA work lowers the clock below the 2.4 GHz of the published
+    peak, so this is the practical ceiling the kernels are compared with."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return dict(kind=f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) operands (vendor GEMM)", reps=reps,
+                ms=round(ms, 4), achieved=round(tf, 2), unit="TFLOP/s",
+                frac_of_peak=round(tf / peak, 4))
 
 
 def selection_rules_report(cfg, q, k, v, o, lse, do, ws, delta, kept_frac, steps):

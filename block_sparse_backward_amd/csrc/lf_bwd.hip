@@ -258,11 +258,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         pld_ok = row < N;
         pld = (tid < kBM ? lse : Drow)[(size_t)bh * N + (pld_ok ? row : N - 1)];
     };
-    // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and D;
-    // rows past N get LSE' = +inf (P = 0) and D = 0, so they add nothing
+    // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and -D
+    // (the start value of the dP products, which then give dP - D); rows past
+    // N get LSE' = +inf (P = 0) and D = 0, so they add nothing
     auto stage_rows = [&](int BF, float lw) {
         if (tid < kBM) sLD[BF][0][tid] = pld_ok ? pld * kLog2e - lw : __builtin_inf();
-        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld_ok ? pld : 0.f;
+        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld_ok ? -pld : 0.f;
     };
     auto stage = [&](int BF, float lw) {
         fq.commit(sQD[BF][0], wave, lane);
@@ -271,11 +272,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     };
     constexpr int NPIECE = decltype(fq)::NPER;
 
-    // S = Q K_w^T and dP = dO V_w^T for one 32-row query tile (A: LDS rows,
-    // B: the K/V fragments in registers)
-    auto sdp = [&](const bf16* sq, const bf16* sdo, int qt, f32x16& s, f32x16& dp, auto&& pre) {
+    // S = Q K_w^T and dP - D = dO V_w^T - D for one 32-row query tile (A:
+    // LDS rows, B: the K/V fragments in registers; the dP products start
+    // from the staged -D of each row, in the accumulator layout)
+    auto sdp = [&](const bf16* sq, const bf16* sdo, const float* snd, int qt, f32x16& s,
+                   f32x16& dp, auto&& pre) {
         pre();  // other work issued alongside (the next sub-tile's loads)
         bf16x8 aq[KS], ao[KS];
+        f32x16 nd;
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(snd + 32 * qt + 8 * a2 + 4 * hf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nd[4 * a2 + e] = x[e];
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             aq[ks] = frag_at<HD>(sq, 32 * qt, off.frag[ks]);
@@ -284,9 +294,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             s = mfma32(aq[ks], kf[ks], ks ? s : zero16);
-            dp = mfma32(ao[ks], vf[ks], ks ? dp : zero16);
+            dp = mfma32(ao[ks], vf[ks], ks ? dp : nd);
         }
-        pipeline_schedule_vmem<2 * KS, 2 * KS, 1, 6, 2 * NPIECE + 1>();
+        pipeline_schedule_vmem<2 * KS + 4, 2 * KS, 1, 10, 2 * NPIECE + 1>();
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -297,14 +307,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     // (opa, oda).  With `SM` false only the dV/dK part runs.
     //   dV_w += P'^T dO,  dK_w += dS'^T Q  (A: P'/dS' in the score layout,
     //   B: transposing LDS reads of the row-major tiles)
-    //   P' = exp2(s scale log2 e - LSE'), zero where the mask hides the pair,
-    //   dS' = P' (dP - D), element (row ql, this lane's key) kept iff ql >= thr
+    //   P' = exp2(s scale log2 e - LSE'),  dS' = P' (dP - D)
+    // (pairs the mask hides are zeroed afterwards by mask_pairs)
     constexpr int kAhead = 3;
     constexpr int NMF = 4 * DT;  // dV/dK MFMAs per 32-row tile
-    auto sm_dvdk = [&](auto SMC, const f32x16& s, const f32x16& dp, const float* sl,
-                       const float* sd, int qt, int thr, bf16x8 (&opa)[2], bf16x8 (&oda)[2],
-                       const bf16* tq, const bf16* tdo, int dqt, const bf16x8 (&ipa)[2],
-                       const bf16x8 (&ida)[2], auto&& extra) {
+    auto sm_dvdk = [&](auto SMC, const f32x16& s, const f32x16& dpd, const float* sl, int qt,
+                       bf16x8 (&opa)[2], bf16x8 (&oda)[2], const bf16* tq, const bf16* tdo,
+                       int dqt, const bf16x8 (&ipa)[2], const bf16x8 (&ida)[2], auto&& extra) {
         constexpr bool SM = decltype(SMC)::value != 0;
         constexpr int EPC = (16 + NMF - 1) / NMF;  // softmax elements per chunk
         auto bfrag = [&](int m) {  // B operand of MFMA m: (half, dt, dV | dK)
@@ -312,14 +321,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
                              off.tr[(m >> 1) % DT]);
         };
         bf16x8 bf[NMF];
-        f32x4 L4[4], D4[4];
+        f32x4 L4[4];
         float pv[16], dsv[16];
         if constexpr (SM) {
 #pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2) {
+            for (int a2 = 0; a2 < 2; ++a2)
                 L4[a2] = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a2 + 4 * hf);
-                D4[a2] = *reinterpret_cast<const f32x4*>(sd + 32 * qt + 8 * a2 + 4 * hf);
-            }
         }
 #pragma unroll
         for (int m = 0; m < kAhead; ++m) bf[m] = bfrag(m);
@@ -330,7 +337,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             if (SM && (m * EPC) % 4 == 0 && (m * EPC) / 4 + 2 < 4) {
                 const int a2 = (m * EPC) / 4 + 2;
                 L4[a2] = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a2 + 4 * hf);
-                D4[a2] = *reinterpret_cast<const f32x4*>(sd + 32 * qt + 8 * a2 + 4 * hf);
             }
             const int half = m / (2 * DT), dt = (m >> 1) % DT;
             if (m & 1) mfma32_agpr(acc_dk[dt], ida[half], bf[m]);
@@ -341,10 +347,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
                     const int r = m * EPC + e;
                     if (r < 16) {
                         const int a2 = r >> 2, bb = r & 3;
-                        float p = fast_exp2(s[r] * scale_log2 - L4[a2][bb]);
-                        if (32 * qt + 8 * a2 + bb < thr) p = 0.f;
+                        const float p = fast_exp2(s[r] * scale_log2 - L4[a2][bb]);
                         pv[r] = p;
-                        dsv[r] = p * (dp[r] - D4[a2][bb]);
+                        dsv[r] = p * dpd[r];
                         if (r & 1) {
                             opa[r >> 3][(r & 7) - 1] = to_bf16(pv[r - 1]);
                             opa[r >> 3][r & 7] = to_bf16(pv[r]);
@@ -362,6 +367,30 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             // their only use is in the next iteration (the compiler would
             // otherwise sink the softmax past the loop's barrier)
             asm volatile("" : "+v"(opa[0]), "+v"(opa[1]), "+v"(oda[0]), "+v"(oda[1]));
+        }
+    };
+
+    // Zero the packed P', dS' of query tile qt where the mask hides the pair:
+    // element r (row 32 qt + 8 (r >> 2) + 4 hf + (r & 3), this lane's key) is
+    // kept iff 32 qt + 8 (r >> 2) + (r & 3) >= thr.  Only sub-tiles on the
+    // causal diagonal or past N need it.
+    auto mask_pairs = [&](int qt, int thr, bf16x8 (&pa)[2], bf16x8 (&da)[2])
+                          __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4 wp = __builtin_bit_cast(u32x4, pa[h]), wd = __builtin_bit_cast(u32x4, da[h]);
+            // a side effect keeps this work behind the branch (the compiler
+            // would otherwise compute the masks on every sub-tile and select)
+            asm volatile("" : "+v"(wp), "+v"(wd));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int r = 8 * h + 2 * w, row = 32 * qt + 8 * (r >> 2) + (r & 3);
+                const uint32_t keep = (row >= thr ? 0xffffu : 0u) | (row + 1 >= thr ? 0xffff0000u : 0u);
+                wp[w] &= keep;
+                wd[w] &= keep;
+            }
+            pa[h] = __builtin_bit_cast(bf16x8, wp);
+            da[h] = __builtin_bit_cast(bf16x8, wd);
         }
     };
 
@@ -394,27 +423,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             const float nx_lw = more ? W.lw : cur_lw;
             // causal: key <= cur_q0 + ql; keys past N are never kept
             const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
+            // the mask hides a pair of this wave's keys and the sub-tile's rows
+            // only on the causal diagonal or past N: elsewhere the softmax skips it
+            const bool wave_masked = __builtin_amdgcn_readfirstlane(
+                (int)(k0 + 32 * wave + 31 >= N || (CAUSAL && cur_q0 < k0 + 32 * wave + 31)));
             const bf16* sq = sQD[buf][0];
             const bf16* sdo = sQD[buf][1];
             const float* sl = sLD[buf][0];
-            const float* sd = sLD[buf][1];
+            const float* snd = sLD[buf][1];
             f32x16 s, dp;
             bf16x8 pa[2], da[2];
             auto nothing = [&](int) {};
             // the next sub-tile's loads go out with this one's first products,
             // and its Q/dO pieces are stored to LDS during the last softmax
-            sdp(sq, sdo, 0, s, dp, [&]() { fetch(nx_bh, nx_q0, nx_lw, fbuf); });
-            sm_dvdk(with_softmax, s, dp, sl, sd, 0, thr, pa, da, sQD[pbuf][0], sQD[pbuf][1], 1,
-                    ppa, pda, nothing);
-            sdp(sq, sdo, 1, s, dp, []() {});
-            sm_dvdk(with_softmax, s, dp, sl, sd, 1, thr, ppa, pda, sq, sdo, 0, pa, da,
-                    [&](int m) {
-                        if ((m & 1) == 0 && m / 2 < 2 * NPIECE) {
-                            const int pc = m / 2;
-                            if (pc < NPIECE) fq.commit_one(sQD[fbuf][0], wave, lane, pc);
-                            else fo.commit_one(sQD[fbuf][1], wave, lane, pc - NPIECE);
-                        }
-                    });
+            sdp(sq, sdo, snd, 0, s, dp, [&]() { fetch(nx_bh, nx_q0, nx_lw, fbuf); });
+            sm_dvdk(with_softmax, s, dp, sl, 0, pa, da, sQD[pbuf][0], sQD[pbuf][1], 1, ppa, pda,
+                    nothing);
+            if (wave_masked) mask_pairs(0, thr, pa, da);
+            sdp(sq, sdo, snd, 1, s, dp, []() {});
+            sm_dvdk(with_softmax, s, dp, sl, 1, ppa, pda, sq, sdo, 0, pa, da, [&](int m) {
+                if ((m & 1) == 0 && m / 2 < 2 * NPIECE) {
+                    const int pc = m / 2;
+                    if (pc < NPIECE) fq.commit_one(sQD[fbuf][0], wave, lane, pc);
+                    else fo.commit_one(sQD[fbuf][1], wave, lane, pc - NPIECE);
+                }
+            });
+            if (wave_masked) mask_pairs(1, thr, ppa, pda);
             stage_rows(fbuf, nx_lw);
             __syncthreads();
             if (!more) break;
@@ -427,8 +461,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         {
             f32x16 s0 = zero16;
             bf16x8 ua[2], ub[2];
-            sm_dvdk(no_softmax, s0, s0, sLD[buf][0], sLD[buf][1], 1, 0, ua, ub, sQD[buf][0],
-                    sQD[buf][1], 1, ppa, pda, [](int) {});
+            sm_dvdk(no_softmax, s0, s0, sLD[buf][0], 1, ua, ub, sQD[buf][0], sQD[buf][1], 1, ppa,
+                    pda, [](int) {});
         }
     }
     // the accumulators were last written by MFMAs the compiler does not see:
