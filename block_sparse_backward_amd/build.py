@@ -18,8 +18,8 @@ SOURCES = ["lf_api.hip", "lf_select.hip", "lf_fwd.hip", "lf_bwd.hip"]
 # the select kernels decide the kept set: no fused multiply-add anywhere there
 EXTRA = {
     "lf_select.hip": ["-ffp-contract=off"],
-    # score products accumulate in VGPRs; the dK/dV accumulators are pinned to
-    # AGPRs in the source, so the two never compete for the same registers
+    # MFMA results stay in VGPRs (no copies between the two register files
+    # around the score products)
     "lf_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

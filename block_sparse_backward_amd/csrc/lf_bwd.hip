@@ -18,18 +18,19 @@
 // Two walks, both deterministic (no floating-point atomics; every sum is
 // taken in a fixed order):
 //
-// dkdv_bf16_kernel -- one workgroup of 4 waves per (batch, kv head, 128-key
-//   tile); wave w owns keys 32w..32w+31 and keeps its K/V fragments and its
-//   dK/dV accumulators in registers for the whole walk.  The workgroup walks
-//   the kept blocks of the Hq/Hkv query heads of its group in 64-row
-//   sub-tiles, software-pipelined over three LDS buffers: the next sub-tile's
-//   Q and dO rows are loaded into registers during the current one's first
-//   products and stored to LDS during its last softmax.  On 32x32x16 bf16
-//   MFMAs: S = Q K_w^T and dP = dO V_w^T (A: LDS rows, B: registers), P' and
-//   dS' in the accumulator layout, then dV_w += P'^T dO and dK_w += dS'^T Q
-//   (A: P' / dS' straight from the score accumulators, B: transposing LDS
-//   reads of the row-major tiles), each softmax interleaved with the dV/dK
-//   products of the neighbouring 32-row tile.
+// dkdv_bf16_kernel -- one workgroup of 8 waves (two per SIMD) per (batch, kv
+//   head, 128-key tile).  Waves w and w + 4 own keys 32 (w & 3) .. + 31 and keep
+//   their K/V fragments in registers for the whole walk; wave w accumulates
+//   dV of those keys, wave w + 4 dK.  The workgroup walks the kept blocks of
+//   the Hq/Hkv query heads of its group in 64-row sub-tiles; of each, the dV
+//   wave computes S = Q K_w^T and dP = dO V_w^T for rows 0..31, the dK wave for
+//   rows 32..63 (32x32x16 bf16 MFMAs, A: LDS rows, B: registers; the dP
+//   products start from -D).  Each turns its scores into P' and dS', keeps
+//   the operand of its own accumulator and sends the other to its partner
+//   through LDS, so dV_w += P'^T dO and dK_w += dS'^T Q each run over all 64
+//   rows (A: P'/dS' in the score layout, B: transposing LDS reads).  One
+//   barrier per sub-tile; the dV/dK products of sub-tile t-1 run alongside
+//   the softmax of t, and the two waves of a SIMD fill each other's stalls.
 //
 // dQ: dq_plan_kernel -> dq_bf16_kernel -> dq_finalize_kernel.  The plan lists
 //   the kept blocks longest first (causal blocks see more keys the later they
@@ -176,36 +177,54 @@ struct Walk {
     __device__ __forceinline__ int q0() const { return i * BLK + st * kBM; }
 };
 
+// dK/dV walk with two waves per SIMD: 8 waves per (batch, kv head, 128-key
+// tile).  Waves w and w + 4 share keys 32 (w & 3) .. + 31 (their K/V
+// fragments in registers); wave w < 4 accumulates dV of those keys and
+// computes S, dP for rows 0..31 of each 64-row sub-tile, wave w + 4
+// accumulates dK and computes rows 32..63.  Each sends its partner the
+// operand the partner lacks (the dV wave its dS', the dK wave its P') through
+// LDS, so each accumulator sees all 64 rows.  Per sub-tile t, between two
+// barriers: S, dP(t) for the wave's rows; then dV or dK of t-1 (own operand
+// for its rows, the partner's for the others; B: transposing reads of t-1's
+// dO or Q) interleaved with the softmax of t; then the exchange.  Q and dO
+// tiles arrive by loads straight to LDS into three named buffers (t-1, t,
+// t+1), the loop unrolled by three so the compiler sees which array each
+// load writes.
 template <int HD, int BLK, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ Drow,
     const int32_t* __restrict__ kept_idx, const int32_t* __restrict__ kept_count,
     const float* __restrict__ block_w, bf16* __restrict__ dk, bf16* __restrict__ dv, int B, int Hq,
     int Hkv, int N, int nqb, float scale, float scale_log2) {
-    constexpr int KS = HD / 16;        // k-steps over the head dim
-    constexpr int DT = HD / 32;        // 32-wide head-dim tiles
-    constexpr int TILE = kBM * HD;     // one staged Q or dO tile (swizzled)
-
-    // staging, three buffers: the sub-tile being computed, the previous one
-    // (its last dV/dK products run alongside this one's first softmax) and the
-    // next one; [buffer][Q | dO], LSE' | D per buffer
-    __shared__ __attribute__((aligned(16))) bf16 sQD[3][2][TILE];
-    __shared__ __attribute__((aligned(16))) float sLD[3][2][kBM];
+    constexpr int KS = HD / 16;     // k-steps over the head dim
+    constexpr int DT = HD / 32;     // 32-wide head-dim tiles
+    constexpr int TILE = kBM * HD;  // one staged Q or dO tile (swizzled)
+    constexpr int NW = 8;
+    __shared__ __attribute__((aligned(16))) bf16 sQ0[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sO0[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sQ1[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sO1[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sQ2[TILE];
+    __shared__ __attribute__((aligned(16))) bf16 sO2[TILE];
+    __shared__ __attribute__((aligned(16))) float sL[3][kBM];  // LSE' per buffer
+    __shared__ __attribute__((aligned(16))) float sN[3][kBM];  // -D per buffer
+    __shared__ __attribute__((aligned(16))) u32x4 sX[2][NW][2][64];  // [parity][sender][half][lane]
 
     int b, g, j;
     map_bwd_block(blockIdx.x, B, Hkv, b, g, j);
     const int G = Hq / Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3;
     const int l32 = lane & 31, hf = lane >> 5;
     const int k0 = j * kBN;
-    const int key = k0 + 32 * wave + l32;  // key column held by this lane
+    const int key = k0 + 32 * kg + l32;  // key column held by this lane
     const bool key_ok = key < N;
     const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)N * HD;
     const f32x16 zero16 = {};
     const TileOffsets<HD> off(lane);
 
-    // ---- K and V fragments: B operands of S = Q K^T and dP = dO V^T
     bf16x8 kf[KS], vf[KS];
     {
         const size_t r = kvoff + (size_t)(key_ok ? key : 0) * HD;
@@ -216,10 +235,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
             if (!key_ok) { kf[ks] = bf16x8{}; vf[ks] = bf16x8{}; }
         }
     }
-
-    f32x16 acc_dk[DT], acc_dv[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) { acc_dk[dt] = zero16; acc_dv[dt] = zero16; }
 
     Walk<BLK, CAUSAL> W;
     W.kept_idx = kept_idx;
@@ -233,158 +248,39 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
     W.g = g;
     W.k0 = k0;
 
-    // A sub-tile's Q and dO rows go straight to LDS; LSE' and D take a
-    // one-register path (they are transformed on the way).
     float pld = 0.f;
-    bool pld_ok = true;  // the staged row exists (the last block may be partial)
+    bool pld_ok = true;
     const uint32_t head_bytes = (uint32_t)N * HD * sizeof(bf16);
-    TileFetch<HD, kBM, 4> fq, fo;
-    auto fetch = [&](int bh, int qs0, float lw, int BF) {
-        (void)lw;
-        (void)BF;
-        // the sub-tile is wave-uniform: keep its offsets scalar (a vector soffset
-        // would turn each buffer load into a loop over distinct values)
+    // a sub-tile's Q and dO rows go straight to LDS; its LSE and D values to
+    // one register (threads 0..63 LSE, the others D, each wave a copy)
+    auto fetch = [&](int bh, int qs0, bf16* tq, bf16* to) __attribute__((always_inline)) {
         bh = __builtin_amdgcn_readfirstlane(bh);
         qs0 = __builtin_amdgcn_readfirstlane(qs0);
         const size_t hoff = (size_t)bh * N * HD;
         const int soff = qs0 * HD * (int)sizeof(bf16);
-        fq.issue(make_rsrc(q + hoff, head_bytes), soff, wave, lane);
-        fo.issue(make_rsrc(dout + hoff, head_bytes), soff, wave, lane);
-        // raw values only: any arithmetic on them here would make the wave wait
-        // for this load, and with it for the tile loads issued just before.
-        // Threads 0..63 load LSE, the others D (two waves load it twice): no
-        // branch, so the loads can share a scheduling region with MFMAs.
+        load_tile_to_lds<HD, kBM, NW>(make_rsrc(q + hoff, head_bytes), soff, tq, wave, lane);
+        load_tile_to_lds<HD, kBM, NW>(make_rsrc(dout + hoff, head_bytes), soff, to, wave, lane);
         const int row = qs0 + (tid & (kBM - 1));
         pld_ok = row < N;
         pld = (tid < kBM ? lse : Drow)[(size_t)bh * N + (pld_ok ? row : N - 1)];
     };
-    // after the tile loads have landed: LSE' = LSE log2 e - log2 w, and -D
-    // (the start value of the dP products, which then give dP - D); rows past
-    // N get LSE' = +inf (P = 0) and D = 0, so they add nothing
-    auto stage_rows = [&](int BF, float lw) {
-        if (tid < kBM) sLD[BF][0][tid] = pld_ok ? pld * kLog2e - lw : __builtin_inf();
-        else if (tid < 2 * kBM) sLD[BF][1][tid - kBM] = pld_ok ? -pld : 0.f;
+    // LSE' = LSE log2 e - log2 w and -D (the start of the dP products); rows
+    // past N get LSE' = +inf (P = 0) and D = 0
+    auto stage_rows = [&](float* sl, float* sn, float lw) __attribute__((always_inline)) {
+        if (tid < kBM) sl[tid] = pld_ok ? pld * kLog2e - lw : __builtin_inf();
+        else if (tid < 2 * kBM) sn[tid - kBM] = pld_ok ? -pld : 0.f;
     };
-    auto stage = [&](int BF, float lw) {
-        fq.commit(sQD[BF][0], wave, lane);
-        fo.commit(sQD[BF][1], wave, lane);
-        stage_rows(BF, lw);
-    };
-    constexpr int NPIECE = decltype(fq)::NPER;
-
-    // S = Q K_w^T and dP - D = dO V_w^T - D for one 32-row query tile (A:
-    // LDS rows, B: the K/V fragments in registers; the dP products start
-    // from the staged -D of each row, in the accumulator layout)
-    auto sdp = [&](const bf16* sq, const bf16* sdo, const float* snd, int qt, f32x16& s,
-                   f32x16& dp, auto&& pre) {
-        pre();  // other work issued alongside (the next sub-tile's loads)
-        bf16x8 aq[KS], ao[KS];
-        f32x16 nd;
-#pragma unroll
-        for (int a2 = 0; a2 < 4; ++a2) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(snd + 32 * qt + 8 * a2 + 4 * hf);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) nd[4 * a2 + e] = x[e];
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            aq[ks] = frag_at<HD>(sq, 32 * qt, off.frag[ks]);
-            ao[ks] = frag_at<HD>(sdo, 32 * qt, off.frag[ks]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = mfma32(aq[ks], kf[ks], ks ? s : zero16);
-            dp = mfma32(ao[ks], vf[ks], ks ? dp : nd);
-        }
-        pipeline_schedule_vmem<2 * KS + 4, 2 * KS, 1, 10, 2 * NPIECE + 1>();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // One softmax and one dV/dK step, interleaved in 4*DT chunks: chunk m
-    // issues the transposing reads of MFMA m + kAhead, runs dV/dK MFMA m of
-    // query tile `dqt` of the tiles (tq, tdo) with the P', dS' operands
-    // (ipa, ida), and turns score elements of query tile `qt` into P' and dS'
-    // (opa, oda).  With `SM` false only the dV/dK part runs.
-    //   dV_w += P'^T dO,  dK_w += dS'^T Q  (A: P'/dS' in the score layout,
-    //   B: transposing LDS reads of the row-major tiles)
-    //   P' = exp2(s scale log2 e - LSE'),  dS' = P' (dP - D)
-    // (pairs the mask hides are zeroed afterwards by mask_pairs)
-    constexpr int kAhead = 3;
-    constexpr int NMF = 4 * DT;  // dV/dK MFMAs per 32-row tile
-    auto sm_dvdk = [&](auto SMC, const f32x16& s, const f32x16& dpd, const float* sl, int qt,
-                       bf16x8 (&opa)[2], bf16x8 (&oda)[2], const bf16* tq, const bf16* tdo,
-                       int dqt, const bf16x8 (&ipa)[2], const bf16x8 (&ida)[2], auto&& extra) {
-        constexpr bool SM = decltype(SMC)::value != 0;
-        constexpr int EPC = (16 + NMF - 1) / NMF;  // softmax elements per chunk
-        auto bfrag = [&](int m) {  // B operand of MFMA m: (half, dt, dV | dK)
-            return tr_at<HD>((m & 1) ? tq : tdo, 32 * dqt + 16 * (m / (2 * DT)),
-                             off.tr[(m >> 1) % DT]);
-        };
-        bf16x8 bf[NMF];
-        f32x4 L4[4];
-        float pv[16], dsv[16];
-        if constexpr (SM) {
-#pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2)
-                L4[a2] = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a2 + 4 * hf);
-        }
-#pragma unroll
-        for (int m = 0; m < kAhead; ++m) bf[m] = bfrag(m);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < NMF; ++m) {
-            if (m + kAhead < NMF) bf[m + kAhead] = bfrag(m + kAhead);
-            if (SM && (m * EPC) % 4 == 0 && (m * EPC) / 4 + 2 < 4) {
-                const int a2 = (m * EPC) / 4 + 2;
-                L4[a2] = *reinterpret_cast<const f32x4*>(sl + 32 * qt + 8 * a2 + 4 * hf);
-            }
-            const int half = m / (2 * DT), dt = (m >> 1) % DT;
-            if (m & 1) mfma32_agpr(acc_dk[dt], ida[half], bf[m]);
-            else mfma32_agpr(acc_dv[dt], ipa[half], bf[m]);
-            if constexpr (SM) {
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    const int r = m * EPC + e;
-                    if (r < 16) {
-                        const int a2 = r >> 2, bb = r & 3;
-                        const float p = fast_exp2(s[r] * scale_log2 - L4[a2][bb]);
-                        pv[r] = p;
-                        dsv[r] = p * dpd[r];
-                        if (r & 1) {
-                            opa[r >> 3][(r & 7) - 1] = to_bf16(pv[r - 1]);
-                            opa[r >> 3][r & 7] = to_bf16(pv[r]);
-                            oda[r >> 3][(r & 7) - 1] = to_bf16(dsv[r - 1]);
-                            oda[r >> 3][r & 7] = to_bf16(dsv[r]);
-                        }
-                    }
-                }
-            }
-            extra(m);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (SM) {
-            // keep P', dS' computed here, interleaved with the MFMAs, even when
-            // their only use is in the next iteration (the compiler would
-            // otherwise sink the softmax past the loop's barrier)
-            asm volatile("" : "+v"(opa[0]), "+v"(opa[1]), "+v"(oda[0]), "+v"(oda[1]));
-        }
-    };
-
-    // Zero the packed P', dS' of query tile qt where the mask hides the pair:
-    // element r (row 32 qt + 8 (r >> 2) + 4 hf + (r & 3), this lane's key) is
-    // kept iff 32 qt + 8 (r >> 2) + (r & 3) >= thr.  Only sub-tiles on the
-    // causal diagonal or past N need it.
-    auto mask_pairs = [&](int qt, int thr, bf16x8 (&pa)[2], bf16x8 (&da)[2])
+    // Zero packed P', dS' of the wave's rows (32 R + 8 (r >> 2) + 4 hf + (r & 3))
+    // where the mask hides the pair: kept iff 32 R + 8 (r >> 2) + (r & 3) >= thr
+    auto mask_pairs = [&](int R, int thr, bf16x8 (&pa)[2], bf16x8 (&da)[2])
                           __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4 wp = __builtin_bit_cast(u32x4, pa[h]), wd = __builtin_bit_cast(u32x4, da[h]);
-            // a side effect keeps this work behind the branch (the compiler
-            // would otherwise compute the masks on every sub-tile and select)
-            asm volatile("" : "+v"(wp), "+v"(wd));
+            asm volatile("" : "+v"(wp), "+v"(wd));  // keeps the work behind the branch
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const int r = 8 * h + 2 * w, row = 32 * qt + 8 * (r >> 2) + (r & 3);
+                const int r = 8 * h + 2 * w, row = 32 * R + 8 * (r >> 2) + (r & 3);
                 const uint32_t keep = (row >= thr ? 0xffffu : 0u) | (row + 1 >= thr ? 0xffff0000u : 0u);
                 wp[w] &= keep;
                 wd[w] &= keep;
@@ -394,93 +290,175 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(
         }
     };
 
-    if (W.first()) {
-        int cur_bh = W.bh, cur_q0 = W.q0();
-        float cur_lw = W.lw;
-        fetch(cur_bh, cur_q0, cur_lw, 0);
-        {   // the "previous" tiles of the first sub-tile hold zeros, so the
-            // pipeline's first dV/dK step (with zero P', dS') adds exact zeros
-            u32x4* z = reinterpret_cast<u32x4*>(&sQD[2][0][0]);
-            for (int c = tid; c < 2 * TILE / 8; c += 256) z[c] = u32x4{};
-        }
-        stage(0, cur_lw);
-        __syncthreads();
-
-        // Pipeline over sub-tiles t (buffer t % 3), two 32-row tiles each:
-        //   S,dP(t,0) | softmax(t,0) + dV,dK(t-1,1) | S,dP(t,1) | softmax(t,1) + dV,dK(t,0)
-        // and dV,dK(last,1) after the walk.
-        const IntC<1> with_softmax;
-        const IntC<0> no_softmax;
-        bf16x8 ppa[2] = {}, pda[2] = {};  // P', dS' of the previous sub-tile's second tile
-        int buf = 0, pbuf = 2;
-        while (true) {
-            const bool more = W.next();
-            const int fbuf = buf == 2 ? 0 : buf + 1;  // the buffer of t-2, free since the barrier
-            // the next sub-tile (this one again after the last: a harmless
-            // reload keeps the loop free of branches)
-            const int nx_bh = more ? W.bh : cur_bh;
-            const int nx_q0 = more ? W.q0() : cur_q0;
-            const float nx_lw = more ? W.lw : cur_lw;
-            // causal: key <= cur_q0 + ql; keys past N are never kept
-            const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
-            // the mask hides a pair of this wave's keys and the sub-tile's rows
-            // only on the causal diagonal or past N: elsewhere the softmax skips it
-            const bool wave_masked = __builtin_amdgcn_readfirstlane(
-                (int)(k0 + 32 * wave + 31 >= N || (CAUSAL && cur_q0 < k0 + 32 * wave + 31)));
-            const bf16* sq = sQD[buf][0];
-            const bf16* sdo = sQD[buf][1];
-            const float* sl = sLD[buf][0];
-            const float* snd = sLD[buf][1];
-            f32x16 s, dp;
-            bf16x8 pa[2], da[2];
-            auto nothing = [&](int) {};
-            // the next sub-tile's loads go out with this one's first products,
-            // and its Q/dO pieces are stored to LDS during the last softmax
-            sdp(sq, sdo, snd, 0, s, dp, [&]() { fetch(nx_bh, nx_q0, nx_lw, fbuf); });
-            sm_dvdk(with_softmax, s, dp, sl, 0, pa, da, sQD[pbuf][0], sQD[pbuf][1], 1, ppa, pda,
-                    nothing);
-            if (wave_masked) mask_pairs(0, thr, pa, da);
-            sdp(sq, sdo, snd, 1, s, dp, []() {});
-            sm_dvdk(with_softmax, s, dp, sl, 1, ppa, pda, sq, sdo, 0, pa, da, [&](int m) {
-                if ((m & 1) == 0 && m / 2 < 2 * NPIECE) {
-                    const int pc = m / 2;
-                    if (pc < NPIECE) fq.commit_one(sQD[fbuf][0], wave, lane, pc);
-                    else fo.commit_one(sQD[fbuf][1], wave, lane, pc - NPIECE);
-                }
-            });
-            if (wave_masked) mask_pairs(1, thr, ppa, pda);
-            stage_rows(fbuf, nx_lw);
+    // The walk of one role (R = 0: dV, rows 0..31; R = 1: dK, rows 32..63).
+    auto walk = [&](auto RC) __attribute__((always_inline)) {
+        constexpr int R = decltype(RC)::value;
+        f32x16 acc[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16;
+        if (W.first()) {
+            int cur_bh = W.bh, cur_q0 = W.q0();
+            float cur_lw = W.lw;
+            fetch(cur_bh, cur_q0, sQ0, sO0);
+            {   // the "previous" sub-tile of the first one: zero rows, zero
+                // exchanged operands, so its dV/dK products add exact zeros
+                u32x4* zq = reinterpret_cast<u32x4*>(sQ2);
+                u32x4* zo = reinterpret_cast<u32x4*>(sO2);
+                for (int c = tid; c < TILE / 8; c += NW * 64) { zq[c] = u32x4{}; zo[c] = u32x4{}; }
+                u32x4* zx = &sX[1][0][0][0];
+                for (int c = tid; c < NW * 2 * 64; c += NW * 64) zx[c] = u32x4{};
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            stage_rows(sL[0], sN[0], cur_lw);
             __syncthreads();
-            if (!more) break;
-            pbuf = buf;
-            buf = fbuf;
-            cur_bh = nx_bh;
-            cur_q0 = nx_q0;
-            cur_lw = nx_lw;
-        }
-        {
-            f32x16 s0 = zero16;
-            bf16x8 ua[2], ub[2];
-            sm_dvdk(no_softmax, s0, s0, sLD[buf][0], 1, ua, ub, sQD[buf][0], sQD[buf][1], 1, ppa,
-                    pda, [](int) {});
-        }
-    }
-    // the accumulators were last written by MFMAs the compiler does not see:
-    // give them their result latency before the epilogue reads them
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // ---- epilogue: dK = scale * acc, dV = acc, bf16
+            constexpr int NMF = 4 * DT;                 // dV or dK MFMAs per sub-tile
+            constexpr int EPC = (16 + NMF - 1) / NMF;   // softmax elements per chunk
+            constexpr int kAhead = 3;
+            bf16x8 own[2] = {};  // this wave's operand of the previous sub-tile
+            int par = 0;         // exchange buffer written by this sub-tile
+            auto iter = [&](const bf16* cq, const bf16* co, const float* cl, const float* cn,
+                            const bf16* pq, const bf16* po, bf16* nq, bf16* no, float* nl,
+                            float* nn) __attribute__((always_inline)) -> bool {
+                const bool more = W.next();
+                // the next sub-tile (this one again after the last: a harmless
+                // reload keeps the iteration free of branches)
+                const int nx_bh = more ? W.bh : cur_bh;
+                const int nx_q0 = more ? W.q0() : cur_q0;
+                const float nx_lw = more ? W.lw : cur_lw;
+                const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
+                const bool wave_masked = __builtin_amdgcn_readfirstlane(
+                    (int)(k0 + 32 * kg + 31 >= N || (CAUSAL && cur_q0 + 32 * R < k0 + 32 * kg + 31)));
+                fetch(nx_bh, nx_q0, nq, no);
+
+                // S = Q K_w^T and dP - D for this wave's 32 rows of sub-tile t
+                f32x16 s, dp;
+                {
+                    bf16x8 aq[KS], ao[KS];
+                    f32x16 nd;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+                    for (int a2 = 0; a2 < 4; ++a2) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(cn + 32 * R + 8 * a2 + 4 * hf);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kr = k0 + 32 * wave + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (kr < N) {
-                const size_t o = kvoff + (size_t)kr * HD + 32 * dt + l32;
-                dk[o] = to_bf16(acc_dk[dt][r] * scale);
-                dv[o] = to_bf16(acc_dv[dt][r]);
+                        for (int e = 0; e < 4; ++e) nd[4 * a2 + e] = x[e];
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        aq[ks] = frag_at<HD>(cq, 32 * R, off.frag[ks]);
+                        ao[ks] = frag_at<HD>(co, 32 * R, off.frag[ks]);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        s = mfma32(aq[ks], kf[ks], ks ? s : zero16);
+                        dp = mfma32(ao[ks], vf[ks], ks ? dp : nd);
+                    }
+                    pipeline_schedule<2 * KS + 4, 2 * KS, 1, 12>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+
+                // dV (R = 0: P'^T dO) or dK (R = 1: dS'^T Q) of sub-tile t-1 over
+                // its 64 rows, with the softmax of t: MFMA m covers row tile qm
+                // (own rows first), 16-row half hm, head-dim tile dm
+                const bf16* tb = R ? pq : po;
+                bf16x8 prt[2];  // the partner's operand, read shortly before its MFMAs
+                auto bfrag = [&](int m) __attribute__((always_inline)) {
+                    const int qm = m < 2 * DT ? R : 1 - R, hm = (m / DT) & 1, dm = m % DT;
+                    return tr_at<HD>(tb, 32 * qm + 16 * hm, off.tr[dm]);
+                };
+                bf16x8 bfr[NMF];
+                f32x4 L4[4];
+                float pv[16], dsv[16];
+                bf16x8 pa[2], da[2];
+#pragma unroll
+                for (int a2 = 0; a2 < 2; ++a2)
+                    L4[a2] = *reinterpret_cast<const f32x4*>(cl + 32 * R + 8 * a2 + 4 * hf);
+#pragma unroll
+                for (int m = 0; m < kAhead; ++m) bfr[m] = bfrag(m);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    if (m + kAhead < NMF) bfr[m + kAhead] = bfrag(m + kAhead);
+                    if (m == 2 * DT - 2) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            prt[h] = __builtin_bit_cast(bf16x8, sX[par ^ 1][wave ^ 4][h][lane]);
+                    }
+                    if ((m * EPC) % 4 == 0 && (m * EPC) / 4 + 2 < 4) {
+                        const int a2 = (m * EPC) / 4 + 2;
+                        L4[a2] = *reinterpret_cast<const f32x4*>(cl + 32 * R + 8 * a2 + 4 * hf);
+                    }
+                    const int hm = (m / DT) & 1, dm = m % DT;
+                    acc[dm] = mfma32(m < 2 * DT ? own[hm] : prt[hm], bfr[m], acc[dm]);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) {
+                        const int r = m * EPC + e;
+                        if (r < 16) {
+                            const int a2 = r >> 2, bb = r & 3;
+                            const float p = fast_exp2(s[r] * scale_log2 - L4[a2][bb]);
+                            pv[r] = p;
+                            dsv[r] = p * dp[r];
+                            if (r & 1) {
+                                pa[r >> 3][(r & 7) - 1] = to_bf16(pv[r - 1]);
+                                pa[r >> 3][r & 7] = to_bf16(pv[r]);
+                                da[r >> 3][(r & 7) - 1] = to_bf16(dsv[r - 1]);
+                                da[r >> 3][r & 7] = to_bf16(dsv[r]);
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                asm volatile("" : "+v"(pa[0]), "+v"(pa[1]), "+v"(da[0]), "+v"(da[1]));
+                if (wave_masked) mask_pairs(R, thr, pa, da);
+                // the partner gets the operand it lacks, this wave keeps its own
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    sX[par][wave][h][lane] = __builtin_bit_cast(u32x4, R ? pa[h] : da[h]);
+                    own[h] = R ? da[h] : pa[h];
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                stage_rows(nl, nn, nx_lw);
+                __syncthreads();
+                par ^= 1;
+                cur_bh = nx_bh;
+                cur_q0 = nx_q0;
+                cur_lw = nx_lw;
+                return more;
+            };
+            int last;
+            while (true) {
+                if (!iter(sQ0, sO0, sL[0], sN[0], sQ2, sO2, sQ1, sO1, sL[1], sN[1])) { last = 0; break; }
+                if (!iter(sQ1, sO1, sL[1], sN[1], sQ0, sO0, sQ2, sO2, sL[2], sN[2])) { last = 1; break; }
+                if (!iter(sQ2, sO2, sL[2], sN[2], sQ1, sO1, sQ0, sO0, sL[0], sN[0])) { last = 2; break; }
+            }
+            // dV or dK of the last sub-tile
+            {
+                const bf16* lq = last == 0 ? sQ0 : last == 1 ? sQ1 : sQ2;
+                const bf16* lo = last == 0 ? sO0 : last == 1 ? sO1 : sO2;
+                const bf16* tb = R ? lq : lo;
+                bf16x8 prt[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    prt[h] = __builtin_bit_cast(bf16x8, sX[par ^ 1][wave ^ 4][h][lane]);
+#pragma unroll
+                for (int m = 0; m < NMF; ++m) {
+                    const int qm = m < 2 * DT ? R : 1 - R, hm = (m / DT) & 1, dm = m % DT;
+                    acc[dm] = mfma32(m < 2 * DT ? own[hm] : prt[hm],
+                                     tr_at<HD>(tb, 32 * qm + 16 * hm, off.tr[dm]), acc[dm]);
+                }
             }
         }
+        bf16* out = R ? dk : dv;
+        const float sc = R ? scale : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kr = k0 + 32 * kg + 8 * (r >> 2) + 4 * hf + (r & 3);
+                if (kr < N) out[kvoff + (size_t)kr * HD + 32 * dt + l32] = to_bf16(acc[dt][r] * sc);
+            }
+    };
+    if (wave >= 4) walk(IntC<1>{});
+    else walk(IntC<0>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1117,7 +1095,7 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
 #define LF_BWD(DD, BB, CC)                                                                      \
     if (pb.d == DD && pb.block == BB && (pb.causal != 0) == CC) {                               \
         if (do_kv)                                                                              \
-            hipLaunchKernelGGL((dkdv_bf16_kernel<DD, BB, CC>), dim3(nwg_kv), dim3(256), 0, st,  \
+            hipLaunchKernelGGL((dkdv_bf16_kernel<DD, BB, CC>), dim3(nwg_kv), dim3(512), 0, st, \
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
                                (const bf16*)dout, D, kept_idx, kept_count, block_w, (bf16*)dk,  \
                                (bf16*)dv, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);    \

@@ -53,35 +53,6 @@ __device__ __forceinline__ void load_tile_to_lds(__amdgpu_buffer_rsrc_t rs, int 
     }
 }
 
-// The same swizzled tile, fetched in two halves through registers: issue()
-// starts this lane's 16-byte loads (coalesced rows), commit() stores them to
-// their swizzled LDS places.  Unlike loads to LDS, a fetch in flight does not
-// hold back the LDS reads of the tile being computed (the compiler cannot tell
-// a load-to-LDS target apart from the tile being read and waits for it).
-template <int HD, int ROWS, int NWAVES>
-struct TileFetch {
-    static constexpr int CPR = HD / 8;
-    static constexpr int NPER = ROWS * CPR / (64 * NWAVES);
-    static_assert(ROWS * CPR % (64 * NWAVES) == 0, "whole rounds");
-    u32x4 r[NPER];
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int soff, int wave, int lane) {
-#pragma unroll
-        for (int m = 0; m < NPER; ++m) {
-            const int S = 64 * (wave + NWAVES * m) + lane;
-            r[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, (S / CPR * HD + S % CPR * 8) * 2, soff, 0);
-        }
-    }
-    __device__ __forceinline__ void commit_one(bf16* lds, int wave, int lane, int m) const {
-        const int S = 64 * (wave + NWAVES * m) + lane;
-        const int row = S / CPR, c = (S % CPR) ^ swz<HD>(row);
-        *reinterpret_cast<u32x4*>(lds + row * HD + c * 8) = r[m];
-    }
-    __device__ __forceinline__ void commit(bf16* lds, int wave, int lane) const {
-#pragma unroll
-        for (int m = 0; m < NPER; ++m) commit_one(lds, wave, lane, m);
-    }
-};
-
 // Per-lane byte offsets into a swizzled tile, fixed for the kernel's life:
 //   frag[ks]    32x32x16 operand fragment of row (R + l32), head-dim chunk
 //               2 ks + hf, for any R that is a multiple of 16;
@@ -160,15 +131,5 @@ template <int V>
 struct IntC {
     static constexpr int value = V;
 };
-
-// acc += a b with the accumulator held in AGPRs for the whole walk (the
-// register allocator otherwise moves accumulator tiles through VGPRs around
-// the score products).  The A operand may have just been written by a VALU
-// op, which needs two wait states before an MFMA reads it; dependent
-// accumulations need none.  The caller waits out the result latency before
-// reading the accumulator with anything but this.
-__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
 
 }  // namespace lf
