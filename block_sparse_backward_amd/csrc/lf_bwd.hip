@@ -559,13 +559,29 @@ __device__ __forceinline__ int block_scan_1024(int x, int* sh, int* total) {
 // step pieces or longer.
 constexpr int kDqMaxChunk = ((kDqChunkBelow - 1) * 8192 + kDqChunkItems - 1) / kDqChunkItems;
 
+constexpr int kDqPlanLds = 16384;  // block weights the plan stages in LDS (64 KiB)
 template <int BLK>
 __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__ block_w, int BHq,
                                                        int nqb, int N, int causal, DqWorkspace ws) {
     __shared__ int sh[32];
     __shared__ int bucket[kDqMaxChunk + 1];  // chunk count, then next queue position, per length
+    __shared__ float sw[kDqPlanLds];
     const int E = BHq * nqb;
     const int tid = threadIdx.x;
+    // the passes below visit the weights in a strided order, four times: read
+    // them once, coalesced, into LDS when they fit
+    const bool staged = E <= kDqPlanLds;
+    if (staged) {
+        for (int x = 4 * tid; x < E; x += 4 * 1024) {
+            if (x + 4 <= E && (E & 3) == 0) {
+                *reinterpret_cast<f32x4*>(&sw[x]) = *reinterpret_cast<const f32x4*>(&block_w[x]);
+            } else {
+                for (int y = x; y < min(E, x + 4); ++y) sw[y] = block_w[y];
+            }
+        }
+        __syncthreads();
+    }
+    auto weight = [&](int blk) { return staged ? sw[blk] : block_w[blk]; };
     const int per = (E + 1023) / 1024;
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
     const int nks = (N + kQN - 1) / kQN;  // key steps of a head (the last may be partial)
@@ -579,7 +595,7 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
     for (int e = e0; e < e1; ++e) {
         int bh, i;
         entry(e, bh, i);
-        if (block_w[(size_t)bh * nqb + i] != 0.f) {
+        if (weight(bh * nqb + i) != 0.f) {
             ++kc;
             ts += steps(i);
         }
@@ -594,7 +610,7 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
     for (int e = e0; e < e1; ++e) {
         int bh, i;
         entry(e, bh, i);
-        if (block_w[(size_t)bh * nqb + i] != 0.f) {
+        if (weight(bh * nqb + i) != 0.f) {
             const int nch = (steps(i) + CL - 1) / CL;
             ni += nch;
             nsl += nch > 1 ? nch : 0;
@@ -613,9 +629,11 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
         for (int e = e0; e < e1; ++e) {
             int bh, i;
             entry(e, bh, i);
-            if (block_w[(size_t)bh * nqb + i] != 0.f) {
+            if (weight(bh * nqb + i) != 0.f) {
                 const int L = steps(i);
-                for (int s0 = 0; s0 < L; s0 += CL) atomicAdd(&bucket[min(CL, L - s0)], 1);
+                const int nch = (L + CL - 1) / CL;
+                for (int c = 0; c < nch; ++c)
+                    atomicAdd(&bucket[((c + 1) * L) / nch - (c * L) / nch], 1);
             }
         }
         __syncthreads();
@@ -645,12 +663,13 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
         entry(e, bh, i);
         const int blk = bh * nqb + i;
         int2 info = make_int2(-1, 0);
-        if (block_w[blk] != 0.f) {
+        if (weight(blk) != 0.f) {
             const int L = steps(i);
             const int nch = (L + CL - 1) / CL;
             info = make_int2(nch > 1 ? sl : -1, nch);
             for (int c = 0; c < nch; ++c) {
-                const int s0 = c * CL, s1 = min(L, s0 + CL);
+                // equal chunks (lengths differ by at most one step)
+                const int s0 = (c * L) / nch, s1 = ((c + 1) * L) / nch;
                 const int at = chunking ? atomicAdd(&bucket[s1 - s0], 1) : it++;
                 ws.items[at] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
             }
@@ -794,8 +813,12 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
             auto step = [&](int t, const bf16* sk, bf16* nxt) {
                 const int kt = NS * t + S;
                 const int k0 = (st0 + kt) * kQN;
-                // key kk of this lane's query is kept iff kk <= lim
+                // key kk of this lane's query is kept iff kk <= lim; only a step
+                // on the causal diagonal (or a stream's missing last step) hides
+                // pairs of this wave, and only then are they zeroed
                 const int lim = kt < nkt ? (CAUSAL ? qrow : 0x7fffffff) : -1;
+                const bool step_masked = __builtin_amdgcn_readfirstlane(
+                    (int)(kt >= nkt || (CAUSAL && k0 + kQN - 1 > i * BLK + 32 * wave)));
                 const bf16* sv = sk + TILE;
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {  // 32-key halves of the step
@@ -823,9 +846,7 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
                         float dsv[16];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            float p = fast_exp2(s[r] * scale_log2 - lse_l);
-                            const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
-                            if (kk > lim) p = 0.f;
+                            const float p = fast_exp2(s[r] * scale_log2 - lse_l);
                             dsv[r] = p * (dp[r] - d_l);
                         }
 #pragma unroll
@@ -834,6 +855,20 @@ __global__ __launch_bounds__(DqShape<BLK>::NT, 2) void dq_bf16_kernel(
 #pragma unroll
                             for (int e = 0; e < 8; ++e) fd[e] = to_bf16(dsv[8 * half + e]);
                             da[half] = fd;
+                        }
+                        if (step_masked) {  // zero the packed dS' of hidden pairs
+#pragma unroll
+                            for (int half = 0; half < 2; ++half) {
+                                u32x4 w = __builtin_bit_cast(u32x4, da[half]);
+                                asm volatile("" : "+v"(w));  // keeps the work behind the branch
+#pragma unroll
+                                for (int c = 0; c < 4; ++c) {
+                                    const int r = 8 * half + 2 * c;
+                                    const int kk = k0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+                                    w[c] &= (kk <= lim ? 0xffffu : 0u) | (kk + 1 <= lim ? 0xffff0000u : 0u);
+                                }
+                                da[half] = __builtin_bit_cast(bf16x8, w);
+                            }
                         }
                     }
                     // dQ += dS' K over these 32 keys; K^T fragments by transposing reads

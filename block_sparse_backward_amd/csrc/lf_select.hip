@@ -218,7 +218,31 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
     // top-k keeps the k largest: k = ceil(f n) (at least 1 for f > 0, n > 0)
     const int topk = min(n, (int)ceil(cnt));
 
-    if (need_sort) {
+    if (need_sort && P <= kSelThreads) {
+        // bitonic sort, ascending (positives first, +inf padding last), one
+        // element per thread: exchanges within a wave (j < 64) by shuffles,
+        // the others through LDS.  The values are finite or +inf, so the pair
+        // (min, max) is the same whichever way a tie is ordered.
+        double x = tid < P ? srt[tid] : 0.0;
+        for (int k = 2; k <= P; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                double y;
+                if (j >= 64) {
+                    __syncthreads();
+                    if (tid < P) srt[tid] = x;
+                    __syncthreads();
+                    y = tid < P ? srt[tid ^ j] : 0.0;
+                } else {
+                    y = __shfl_xor(x, j);
+                }
+                const bool low = (tid & j) == 0, up = (tid & k) == 0;
+                x = (low == up) ? fmin(x, y) : fmax(x, y);
+            }
+        }
+        __syncthreads();
+        if (tid < P) srt[tid] = x;
+        __syncthreads();
+    } else if (need_sort) {
         // bitonic sort, ascending (positives first, +inf padding last)
         for (int k = 2; k <= P; k <<= 1) {
             for (int j = k >> 1; j > 0; j >>= 1) {
@@ -240,7 +264,20 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
         // sequential running sums in ascending order (one rounding per op)
         if (tid == 0) {
             double a = 0.0, q = 0.0;
-            for (int k = 0; k < n; ++k) {
+            int k = 0;
+            for (; k + 8 <= n; k += 8) {  // the next 8 masses read ahead of the chain
+                double mk[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) mk[u] = srt[k + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    a = __dadd_rn(a, mk[u]);
+                    q = __dadd_rn(q, __dmul_rn(mk[u], mk[u]));
+                    accA[k + u] = a;
+                    accQ[k + u] = q;
+                }
+            }
+            for (; k < n; ++k) {
                 const double mk = srt[k];
                 a = __dadd_rn(a, mk);
                 q = __dadd_rn(q, __dmul_rn(mk, mk));
