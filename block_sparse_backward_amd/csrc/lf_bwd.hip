@@ -523,32 +523,43 @@ __host__ __device__ inline DqWorkspace dq_workspace(void* base, size_t nblocks, 
     return w;
 }
 
-// Block-wide exclusive scan of one int per thread (1024 threads); returns the
-// prefix and writes the total to *total.
-__device__ __forceinline__ int block_scan_1024(int x, int* sh, int* total) {
+// Block-wide exclusive scans of M ints per thread (1024 threads) at once:
+// x[m] becomes its exclusive prefix and total[m] the sum.  `sh` holds
+// 17 M ints.
+template <int M>
+__device__ __forceinline__ void block_scan_1024(int (&x)[M], int* sh, int (&total)[M]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = x;
+    int inc[M];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
-    }
-    if (lane == 63) sh[wave] = inc;
+    for (int m = 0; m < M; ++m) inc[m] = x[m];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int y = __shfl_up(inc[m], off);
+            if (lane >= off) inc[m] += y;
+        }
+    if (lane == 63)
+#pragma unroll
+        for (int m = 0; m < M; ++m) sh[17 * m + wave] = inc[m];
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < M) {
+        int* q = sh + 17 * threadIdx.x;
         int run = 0;
         for (int w = 0; w < 16; ++w) {
-            const int t = sh[w];
-            sh[w] = run;
+            const int t = q[w];
+            q[w] = run;
             run += t;
         }
-        sh[16] = run;
+        q[16] = run;
     }
     __syncthreads();
-    const int r = sh[wave] + inc - x;
-    *total = sh[16];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        total[m] = sh[17 * m + 16];
+        x[m] = sh[17 * m + wave] + inc[m] - x[m];
+    }
     __syncthreads();
-    return r;
 }
 
 // One workgroup of 1024 threads.  Entries e = 0 .. E-1 run over (block i
@@ -563,7 +574,7 @@ constexpr int kDqPlanLds = 16384;  // block weights the plan stages in LDS (64 K
 template <int BLK>
 __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__ block_w, int BHq,
                                                        int nqb, int N, int causal, DqWorkspace ws) {
-    __shared__ int sh[32];
+    __shared__ int sh[17 * 3];
     __shared__ int bucket[kDqMaxChunk + 1];  // chunk count, then next queue position, per length
     __shared__ float sw[kDqPlanLds];
     const int E = BHq * nqb;
@@ -581,118 +592,124 @@ __global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__
         }
         __syncthreads();
     }
-    auto weight = [&](int blk) { return staged ? sw[blk] : block_w[blk]; };
-    const int per = (E + 1023) / 1024;
-    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-    const int nks = (N + kQN - 1) / kQN;  // key steps of a head (the last may be partial)
-    auto steps = [&](int i) { return causal ? min((i * BLK + BLK - 1) / kQN + 1, nks) : nks; };
-    auto entry = [&](int e, int& bh, int& i) {
-        i = nqb - 1 - e / BHq;
-        bh = e % BHq;
-    };
-    // pass 1: kept blocks K and their total key steps T
-    int kc = 0, ts = 0;
-    for (int e = e0; e < e1; ++e) {
-        int bh, i;
-        entry(e, bh, i);
-        if (weight(bh * nqb + i) != 0.f) {
-            ++kc;
-            ts += steps(i);
-        }
-    }
-    int K, T;
-    const int kpre = block_scan_1024(kc, sh, &K);
-    block_scan_1024(ts, sh, &T);
-    const bool chunking = K < kDqChunkBelow;
-    const int CL = chunking ? max(kDqMinChunk, (T + kDqChunkItems - 1) / kDqChunkItems) : (1 << 30);
-    // pass 2: compute items, partial slots and chunked blocks per thread
-    int ni = 0, nsl = 0, nck = 0;
-    for (int e = e0; e < e1; ++e) {
-        int bh, i;
-        entry(e, bh, i);
-        if (weight(bh * nqb + i) != 0.f) {
-            const int nch = (steps(i) + CL - 1) / CL;
-            ni += nch;
-            nsl += nch > 1 ? nch : 0;
-            nck += nch > 1;
-        }
-    }
-    int n_items, n_slots, n_chunked;
-    int it = block_scan_1024(ni, sh, &n_items);
-    int sl = block_scan_1024(nsl, sh, &n_slots);
-    int ck = block_scan_1024(nck, sh, &n_chunked);
-    if (chunking) {
-        // Queue order longest first over all chunks (not block by block): a
-        // counting sort by chunk length, so short remainders end the queue.
-        for (int c = tid; c <= CL; c += 1024) bucket[c] = 0;
-        __syncthreads();
+    // one copy of the plan per source of the weights, so each reads its own
+    // address space (a choice between the two would read through flat loads)
+    auto plan = [&](auto weight) __attribute__((always_inline)) {
+        const int per = (E + 1023) / 1024;
+        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+        const int nks = (N + kQN - 1) / kQN;  // key steps of a head (the last may be partial)
+        auto steps = [&](int i) { return causal ? min((i * BLK + BLK - 1) / kQN + 1, nks) : nks; };
+        auto entry = [&](int e, int& bh, int& i) {
+            i = nqb - 1 - e / BHq;
+            bh = e % BHq;
+        };
+        // pass 1: kept blocks K and their total key steps T
+        int kc = 0, ts = 0;
         for (int e = e0; e < e1; ++e) {
             int bh, i;
             entry(e, bh, i);
             if (weight(bh * nqb + i) != 0.f) {
+                ++kc;
+                ts += steps(i);
+            }
+        }
+        int kt2[2] = {kc, ts}, tot2[2];
+        block_scan_1024(kt2, sh, tot2);
+        const int kpre = kt2[0], K = tot2[0], T = tot2[1];
+        const bool chunking = K < kDqChunkBelow;
+        const int CL = chunking ? max(kDqMinChunk, (T + kDqChunkItems - 1) / kDqChunkItems) : (1 << 30);
+        // pass 2: compute items, partial slots and chunked blocks per thread
+        int ni = 0, nsl = 0, nck = 0;
+        for (int e = e0; e < e1; ++e) {
+            int bh, i;
+            entry(e, bh, i);
+            if (weight(bh * nqb + i) != 0.f) {
+                const int nch = (steps(i) + CL - 1) / CL;
+                ni += nch;
+                nsl += nch > 1 ? nch : 0;
+                nck += nch > 1;
+            }
+        }
+        int isc[3] = {ni, nsl, nck}, itot[3];
+        block_scan_1024(isc, sh, itot);
+        int it = isc[0], sl = isc[1], ck = isc[2];
+        const int n_items = itot[0], n_chunked = itot[2];
+        if (chunking) {
+            // Queue order longest first over all chunks (not block by block): a
+            // counting sort by chunk length, so short remainders end the queue.
+            for (int c = tid; c <= CL; c += 1024) bucket[c] = 0;
+            __syncthreads();
+            for (int e = e0; e < e1; ++e) {
+                int bh, i;
+                entry(e, bh, i);
+                if (weight(bh * nqb + i) != 0.f) {
+                    const int L = steps(i);
+                    const int nch = (L + CL - 1) / CL;
+                    for (int c = 0; c < nch; ++c)
+                        atomicAdd(&bucket[((c + 1) * L) / nch - (c * L) / nch], 1);
+                }
+            }
+            __syncthreads();
+            // exclusive prefix over lengths, longest first: bucket[len] = first
+            // queue position of its chunks
+            constexpr int PER = (kDqMaxChunk + 1 + 1023) / 1024;
+            int cnt[PER], tot = 0;
+    #pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int len = CL - (tid * PER + u);
+                cnt[u] = len >= 1 ? bucket[len] : 0;
+                tot += cnt[u];
+            }
+            int run1[1] = {tot}, all[1];
+            block_scan_1024(run1, sh, all);
+            int run = run1[0];
+    #pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int len = CL - (tid * PER + u);
+                if (len >= 1) bucket[len] = run;
+                run += cnt[u];
+            }
+            __syncthreads();
+        }
+        int sk = e0 - kpre;  // skipped blocks before this thread's entries
+        for (int e = e0; e < e1; ++e) {
+            int bh, i;
+            entry(e, bh, i);
+            const int blk = bh * nqb + i;
+            int2 info = make_int2(-1, 0);
+            if (weight(blk) != 0.f) {
                 const int L = steps(i);
                 const int nch = (L + CL - 1) / CL;
-                for (int c = 0; c < nch; ++c)
-                    atomicAdd(&bucket[((c + 1) * L) / nch - (c * L) / nch], 1);
+                info = make_int2(nch > 1 ? sl : -1, nch);
+                for (int c = 0; c < nch; ++c) {
+                    // equal chunks (lengths differ by at most one step)
+                    const int s0 = (c * L) / nch, s1 = ((c + 1) * L) / nch;
+                    const int at = chunking ? atomicAdd(&bucket[s1 - s0], 1) : it++;
+                    ws.items[at] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
+                }
+                if (nch > 1) {
+                    sl += nch;
+                    ws.chunked[ck++] = blk;
+                }
+            } else {
+                ws.skip[sk++] = blk;
             }
+            ws.blk[blk] = info;
         }
-        __syncthreads();
-        // exclusive prefix over lengths, longest first: bucket[len] = first
-        // queue position of its chunks
-        constexpr int PER = (kDqMaxChunk + 1 + 1023) / 1024;
-        int cnt[PER], tot = 0;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int len = CL - (tid * PER + u);
-            cnt[u] = len >= 1 ? bucket[len] : 0;
-            tot += cnt[u];
+        // zero-fill items go last: they take up the walk's tail
+        const int n_skip = E - K;
+        const int n_zero = (n_skip + kDqZeroPer - 1) / kDqZeroPer;
+        for (int z = tid; z < n_zero; z += 1024)
+            ws.items[n_items + z] =
+                make_int4(-1, z * kDqZeroPer, min(kDqZeroPer, n_skip - z * kDqZeroPer), 0);
+        if (tid == 0) {
+            ws.ctrl[0] = n_items + n_zero;
+            ws.ctrl[1] = 0;
+            ws.ctrl[2] = n_chunked;
         }
-        int all;
-        int run = block_scan_1024(tot, sh, &all);
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int len = CL - (tid * PER + u);
-            if (len >= 1) bucket[len] = run;
-            run += cnt[u];
-        }
-        __syncthreads();
-    }
-    int sk = e0 - kpre;  // skipped blocks before this thread's entries
-    for (int e = e0; e < e1; ++e) {
-        int bh, i;
-        entry(e, bh, i);
-        const int blk = bh * nqb + i;
-        int2 info = make_int2(-1, 0);
-        if (weight(blk) != 0.f) {
-            const int L = steps(i);
-            const int nch = (L + CL - 1) / CL;
-            info = make_int2(nch > 1 ? sl : -1, nch);
-            for (int c = 0; c < nch; ++c) {
-                // equal chunks (lengths differ by at most one step)
-                const int s0 = (c * L) / nch, s1 = ((c + 1) * L) / nch;
-                const int at = chunking ? atomicAdd(&bucket[s1 - s0], 1) : it++;
-                ws.items[at] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
-            }
-            if (nch > 1) {
-                sl += nch;
-                ws.chunked[ck++] = blk;
-            }
-        } else {
-            ws.skip[sk++] = blk;
-        }
-        ws.blk[blk] = info;
-    }
-    // zero-fill items go last: they take up the walk's tail
-    const int n_skip = E - K;
-    const int n_zero = (n_skip + kDqZeroPer - 1) / kDqZeroPer;
-    for (int z = tid; z < n_zero; z += 1024)
-        ws.items[n_items + z] =
-            make_int4(-1, z * kDqZeroPer, min(kDqZeroPer, n_skip - z * kDqZeroPer), 0);
-    if (tid == 0) {
-        ws.ctrl[0] = n_items + n_zero;
-        ws.ctrl[1] = 0;
-        ws.ctrl[2] = n_chunked;
-    }
+    };
+    if (staged) plan([&](int blk) { return sw[blk]; });
+    else plan([&](int blk) { return block_w[blk]; });
 }
 
 // Persistent dQ walk.  Each item is one kept block's key steps [s0, s1).  A
