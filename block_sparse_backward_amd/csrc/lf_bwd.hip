@@ -177,6 +177,281 @@ struct Walk {
     __device__ __forceinline__ int q0() const { return i * BLK + st * kBM; }
 };
 
+// ---------------------------------------------------------------------------
+// dQ phase (bf16): plan -> persistent walk -> finalize.
+//
+// The work of a kept block is its key steps (64 keys each) that the causal mask
+// lets it see, so block lengths differ by up to nqb x.  With few kept blocks
+// the longest block would set the run time, so when fewer than 2 * kDqGrid
+// blocks are kept the plan cuts blocks into chunks of about equal length and
+// the chunks' fp32 partials are added in a fixed order by the finalize pass
+// (deterministic).  The persistent kernel takes items from a queue, longest
+// blocks first.
+// ---------------------------------------------------------------------------
+constexpr int kDqGrid = 256;                 // persistent workgroups (one per CU)
+constexpr int kDqChunkItems = 4 * kDqGrid;   // chunking aims at about this many chunks
+constexpr int kDqMaxSlots = kDqChunkItems + 2 * kDqGrid;  // fp32 partial tiles, see dq_plan_kernel
+constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
+constexpr int kDqChunkBelow = 2 * kDqGrid;   // chunk blocks when fewer are kept
+constexpr int kDqZeroPer = 8;                // skipped blocks per zero-fill item
+constexpr int kDqFinSplit = 2;               // finalize workgroups per chunked block
+
+struct DqWorkspace {  // carved out of the caller's workspace
+    int* ctrl;        // [0] items, [1] queue position, [2] chunked blocks
+    int4* items;      // compute: {bh, block, first step | end step << 16, partial slot or -1}
+                      // zero fill: {-1, first skipped-list entry, entries, 0}
+    int2* blk;        // per (bh, block): {first slot or -1, chunks}
+    int* skip;        // skipped blocks, (bh, block) in memory order
+    int* chunked;     // blocks cut into chunks
+    float* part;      // [kDqMaxSlots][BLK * HD]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// compute items: one per kept block, or (chunking) at most 2 T / CL <= kDqMaxSlots
+// chunks plus one per block; zero-fill items: one per kDqZeroPer skipped blocks
+__host__ __device__ inline size_t dq_max_items(size_t nblocks) {
+    return nblocks + (size_t)kDqMaxSlots + nblocks / kDqZeroPer + 1;
+}
+
+__host__ __device__ inline size_t dq_workspace_bytes(size_t nblocks, int blk, int hd) {
+    return align256(64 * sizeof(int)) + align256(dq_max_items(nblocks) * sizeof(int4)) +
+           align256(nblocks * sizeof(int2)) + align256(nblocks * sizeof(int)) +
+           align256(kDqChunkBelow * sizeof(int)) + (size_t)kDqMaxSlots * blk * hd * sizeof(float);
+}
+
+__host__ __device__ inline DqWorkspace dq_workspace(void* base, size_t nblocks, int blk, int hd) {
+    char* p = static_cast<char*>(base);
+    DqWorkspace w;
+    w.ctrl = reinterpret_cast<int*>(p);
+    p += align256(64 * sizeof(int));
+    w.items = reinterpret_cast<int4*>(p);
+    p += align256(dq_max_items(nblocks) * sizeof(int4));
+    w.blk = reinterpret_cast<int2*>(p);
+    p += align256(nblocks * sizeof(int2));
+    w.skip = reinterpret_cast<int*>(p);
+    p += align256(nblocks * sizeof(int));
+    w.chunked = reinterpret_cast<int*>(p);
+    p += align256(kDqChunkBelow * sizeof(int));
+    w.part = reinterpret_cast<float*>(p);
+    (void)blk;
+    (void)hd;
+    return w;
+}
+
+// Block-wide exclusive scans of M ints per thread (NT threads) at once:
+// x[m] becomes its exclusive prefix and total[m] the sum.  `sh` holds
+// (NT / 64 + 1) M ints.
+template <int NT, int M>
+__device__ __forceinline__ void block_scan(int (&x)[M], int* sh, int (&total)[M]) {
+    constexpr int NW = NT / 64, SP = NW + 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) inc[m] = x[m];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int y = __shfl_up(inc[m], off);
+            if (lane >= off) inc[m] += y;
+        }
+    if (lane == 63)
+#pragma unroll
+        for (int m = 0; m < M; ++m) sh[SP * m + wave] = inc[m];
+    __syncthreads();
+    if (threadIdx.x < M) {
+        int* q = sh + SP * threadIdx.x;
+        int run = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int t = q[w];
+            q[w] = run;
+            run += t;
+        }
+        q[NW] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        total[m] = sh[SP * m + NW];
+        x[m] = sh[SP * m + wave] + inc[m] - x[m];
+    }
+    __syncthreads();
+}
+
+// One workgroup of 1024 threads.  Entries e = 0 .. E-1 run over (block i
+// descending, head bh ascending); an entry is kept when its block weight is
+// non-zero.  Emits the items in that order and the per-block slot table.
+// Chunk lengths never exceed this many key steps: chunking happens with fewer
+// than kDqChunkBelow kept blocks of at most 8192 steps, cut into T / kDqChunkItems
+// step pieces or longer.
+constexpr int kDqMaxChunk = ((kDqChunkBelow - 1) * 8192 + kDqChunkItems - 1) / kDqChunkItems;
+
+constexpr int kDqPlanLds = 16384;  // block weights the plan stages in LDS (64 KiB)
+constexpr int kDqBucketInts = kDqMaxChunk + 1;
+// The plan, run by one workgroup of NT threads.  LDS: `sw` (swcap floats; the
+// weights are staged there when they fit), `bucket` (kDqBucketInts ints: chunk
+// count, then next queue position, per length) and `sh` (3 (NT / 64 + 1) ints).
+template <int BLK, int NT>
+__device__ __forceinline__ void dq_plan_body(const float* __restrict__ block_w, int BHq, int nqb,
+                                             int N, int causal, DqWorkspace ws, float* sw,
+                                             int swcap, int* bucket, int* sh) {
+    const int E = BHq * nqb;
+    const int tid = threadIdx.x;
+    // the passes below visit the weights in a strided order, four times: read
+    // them once, coalesced, into LDS when they fit
+    const bool staged = E <= swcap;
+    if (staged) {
+        for (int x = 4 * tid; x < E; x += 4 * NT) {
+            if (x + 4 <= E && (E & 3) == 0) {
+                *reinterpret_cast<f32x4*>(&sw[x]) = *reinterpret_cast<const f32x4*>(&block_w[x]);
+            } else {
+                for (int y = x; y < min(E, x + 4); ++y) sw[y] = block_w[y];
+            }
+        }
+        __syncthreads();
+    }
+    // one copy of the plan per source of the weights, so each reads its own
+    // address space (a choice between the two would read through flat loads)
+    auto plan = [&](auto weight) __attribute__((always_inline)) {
+        const int per = (E + NT - 1) / NT;
+        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+        const int nks = (N + kQN - 1) / kQN;  // key steps of a head (the last may be partial)
+        auto steps = [&](int i) { return causal ? min((i * BLK + BLK - 1) / kQN + 1, nks) : nks; };
+        auto entry = [&](int e, int& bh, int& i) {
+            i = nqb - 1 - e / BHq;
+            bh = e % BHq;
+        };
+        // pass 1: kept blocks K and their total key steps T
+        int kc = 0, ts = 0;
+        for (int e = e0; e < e1; ++e) {
+            int bh, i;
+            entry(e, bh, i);
+            if (weight(bh * nqb + i) != 0.f) {
+                ++kc;
+                ts += steps(i);
+            }
+        }
+        int kt2[2] = {kc, ts}, tot2[2];
+        block_scan<NT>(kt2, sh, tot2);
+        const int kpre = kt2[0], K = tot2[0], T = tot2[1];
+        const bool chunking = K < kDqChunkBelow;
+        const int CL = chunking ? max(kDqMinChunk, (T + kDqChunkItems - 1) / kDqChunkItems) : (1 << 30);
+        // pass 2: compute items, partial slots and chunked blocks per thread
+        int ni = 0, nsl = 0, nck = 0;
+        for (int e = e0; e < e1; ++e) {
+            int bh, i;
+            entry(e, bh, i);
+            if (weight(bh * nqb + i) != 0.f) {
+                const int nch = (steps(i) + CL - 1) / CL;
+                ni += nch;
+                nsl += nch > 1 ? nch : 0;
+                nck += nch > 1;
+            }
+        }
+        int isc[3] = {ni, nsl, nck}, itot[3];
+        block_scan<NT>(isc, sh, itot);
+        int it = isc[0], sl = isc[1], ck = isc[2];
+        const int n_items = itot[0], n_chunked = itot[2];
+        if (chunking) {
+            // Queue order longest first over all chunks (not block by block): a
+            // counting sort by chunk length, so short remainders end the queue.
+            for (int c = tid; c <= CL; c += NT) bucket[c] = 0;
+            __syncthreads();
+            for (int e = e0; e < e1; ++e) {
+                int bh, i;
+                entry(e, bh, i);
+                if (weight(bh * nqb + i) != 0.f) {
+                    const int L = steps(i);
+                    const int nch = (L + CL - 1) / CL;
+                    for (int c = 0; c < nch; ++c)
+                        atomicAdd(&bucket[((c + 1) * L) / nch - (c * L) / nch], 1);
+                }
+            }
+            __syncthreads();
+            // exclusive prefix over lengths, longest first: bucket[len] = first
+            // queue position of its chunks
+            constexpr int PER = (kDqBucketInts + NT - 1) / NT;
+            int cnt[PER], tot = 0;
+    #pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int len = CL - (tid * PER + u);
+                cnt[u] = len >= 1 ? bucket[len] : 0;
+                tot += cnt[u];
+            }
+            int run1[1] = {tot}, all[1];
+            block_scan<NT>(run1, sh, all);
+            int run = run1[0];
+    #pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int len = CL - (tid * PER + u);
+                if (len >= 1) bucket[len] = run;
+                run += cnt[u];
+            }
+            __syncthreads();
+        }
+        int sk = e0 - kpre;  // skipped blocks before this thread's entries
+        for (int e = e0; e < e1; ++e) {
+            int bh, i;
+            entry(e, bh, i);
+            const int blk = bh * nqb + i;
+            int2 info = make_int2(-1, 0);
+            if (weight(blk) != 0.f) {
+                const int L = steps(i);
+                const int nch = (L + CL - 1) / CL;
+                info = make_int2(nch > 1 ? sl : -1, nch);
+                for (int c = 0; c < nch; ++c) {
+                    // equal chunks (lengths differ by at most one step)
+                    const int s0 = (c * L) / nch, s1 = ((c + 1) * L) / nch;
+                    const int at = chunking ? atomicAdd(&bucket[s1 - s0], 1) : it++;
+                    ws.items[at] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
+                }
+                if (nch > 1) {
+                    sl += nch;
+                    ws.chunked[ck++] = blk;
+                }
+            } else {
+                ws.skip[sk++] = blk;
+            }
+            ws.blk[blk] = info;
+        }
+        // zero-fill items go last: they take up the walk's tail
+        const int n_skip = E - K;
+        const int n_zero = (n_skip + kDqZeroPer - 1) / kDqZeroPer;
+        for (int z = tid; z < n_zero; z += NT)
+            ws.items[n_items + z] =
+                make_int4(-1, z * kDqZeroPer, min(kDqZeroPer, n_skip - z * kDqZeroPer), 0);
+        if (tid == 0) {
+            ws.ctrl[0] = n_items + n_zero;
+            ws.ctrl[1] = 0;
+            ws.ctrl[2] = n_chunked;
+        }
+    };
+    if (staged) plan([&](int blk) { return sw[blk]; });
+    else plan([&](int blk) { return block_w[blk]; });
+}
+
+template <int BLK>
+__global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__ block_w, int BHq,
+                                                       int nqb, int N, int causal, DqWorkspace ws) {
+    __shared__ int sh[3 * 17];
+    __shared__ int bucket[kDqBucketInts];
+    __shared__ float sw[kDqPlanLds];
+    dq_plan_body<BLK, 1024>(block_w, BHq, nqb, N, causal, ws, sw, kDqPlanLds, bucket, sh);
+}
+
+// Persistent dQ walk.  Each item is one kept block's key steps [s0, s1).  A
+// workgroup has 4 waves of 32 query rows: for 128-row blocks one stream of 4
+// waves takes every step (two workgroups per CU); for 64-row blocks two
+// streams of 2 waves split the steps, even to stream 0 and odd to stream 1,
+// and add their partials in LDS at the end.  The result goes to the dq rows
+// (single-chunk block) or to the item's fp32 partial slot.  Each stream
+// double-buffers its K/V tiles in two LDS arrays of its own, and the code of
+// each stream and buffer names its arrays at compile time: loads to LDS into
+// one array then never hold back the LDS reads of another (the compiler waits
+// for a load to LDS before reading the same array).  The next step's loads go
+// out among the current step's score MFMAs.  Steps run without branches: keys
+// the causal mask hides, and a stream's missing last step, add exact zeros.
 // dK/dV walk with two waves per SIMD: 8 waves per (batch, kv head, 128-key
 // tile).  Waves w and w + 4 share keys 32 (w & 3) .. + 31 (their K/V
 // fragments in registers); wave w < 4 accumulates dV of those keys and
@@ -189,14 +464,16 @@ struct Walk {
 // dO or Q) interleaved with the softmax of t; then the exchange.  Q and dO
 // tiles arrive by loads straight to LDS into three named buffers (t-1, t,
 // t+1), the loop unrolled by three so the compiler sees which array each
-// load writes.
-template <int HD, int BLK, bool CAUSAL>
+// load writes.  With PLAN, workgroup 0 instead runs the dQ plan (on this
+// kernel's LDS) while the others walk, so the plan costs the walk one CU for
+// its run time rather than a launch of its own.
+template <int HD, int BLK, bool CAUSAL, bool PLAN>
 __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ Drow,
     const int32_t* __restrict__ kept_idx, const int32_t* __restrict__ kept_count,
     const float* __restrict__ block_w, bf16* __restrict__ dk, bf16* __restrict__ dv, int B, int Hq,
-    int Hkv, int N, int nqb, float scale, float scale_log2) {
+    int Hkv, int N, int nqb, float scale, float scale_log2, DqWorkspace ws) {
     constexpr int KS = HD / 16;     // k-steps over the head dim
     constexpr int DT = HD / 32;     // 32-wide head-dim tiles
     constexpr int TILE = kBM * HD;  // one staged Q or dO tile (swizzled)
@@ -211,8 +488,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     __shared__ __attribute__((aligned(16))) float sN[3][kBM];  // -D per buffer
     __shared__ __attribute__((aligned(16))) u32x4 sX[2][NW][2][64];  // [parity][sender][half][lane]
 
+    if constexpr (PLAN) {
+        static_assert(sizeof(sQ0) >= kDqBucketInts * sizeof(int), "plan buckets fit one tile");
+        static_assert(sizeof(sL) >= 3 * (NW + 1) * sizeof(int), "plan scan space");
+        if (blockIdx.x == 0) {
+            dq_plan_body<BLK, NW * 64>(block_w, B * Hq, nqb, N, CAUSAL, ws,
+                                       reinterpret_cast<float*>(&sX[0][0][0][0]),
+                                       (int)(sizeof(sX) / sizeof(float)),
+                                       reinterpret_cast<int*>(sQ0), &reinterpret_cast<int*>(sL)[0]);
+            return;
+        }
+    }
     int b, g, j;
-    map_bwd_block(blockIdx.x, B, Hkv, b, g, j);
+    map_bwd_block(blockIdx.x - (PLAN ? 1 : 0), B, Hkv, b, g, j);
     const int G = Hq / Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,269 +749,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     else walk(IntC<0>{});
 }
 
-// ---------------------------------------------------------------------------
-// dQ phase (bf16): plan -> persistent walk -> finalize.
-//
-// The work of a kept block is its key steps (64 keys each) that the causal mask
-// lets it see, so block lengths differ by up to nqb x.  With few kept blocks
-// the longest block would set the run time, so when fewer than 2 * kDqGrid
-// blocks are kept the plan cuts blocks into chunks of about equal length and
-// the chunks' fp32 partials are added in a fixed order by the finalize pass
-// (deterministic).  The persistent kernel takes items from a queue, longest
-// blocks first.
-// ---------------------------------------------------------------------------
-constexpr int kDqGrid = 256;                 // persistent workgroups (one per CU)
-constexpr int kDqChunkItems = 4 * kDqGrid;   // chunking aims at about this many chunks
-constexpr int kDqMaxSlots = kDqChunkItems + 2 * kDqGrid;  // fp32 partial tiles, see dq_plan_kernel
-constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
-constexpr int kDqChunkBelow = 2 * kDqGrid;   // chunk blocks when fewer are kept
-constexpr int kDqZeroPer = 8;                // skipped blocks per zero-fill item
-constexpr int kDqFinSplit = 2;               // finalize workgroups per chunked block
-
-struct DqWorkspace {  // carved out of the caller's workspace
-    int* ctrl;        // [0] items, [1] queue position, [2] chunked blocks
-    int4* items;      // compute: {bh, block, first step | end step << 16, partial slot or -1}
-                      // zero fill: {-1, first skipped-list entry, entries, 0}
-    int2* blk;        // per (bh, block): {first slot or -1, chunks}
-    int* skip;        // skipped blocks, (bh, block) in memory order
-    int* chunked;     // blocks cut into chunks
-    float* part;      // [kDqMaxSlots][BLK * HD]
-};
-
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// compute items: one per kept block, or (chunking) at most 2 T / CL <= kDqMaxSlots
-// chunks plus one per block; zero-fill items: one per kDqZeroPer skipped blocks
-__host__ __device__ inline size_t dq_max_items(size_t nblocks) {
-    return nblocks + (size_t)kDqMaxSlots + nblocks / kDqZeroPer + 1;
-}
-
-__host__ __device__ inline size_t dq_workspace_bytes(size_t nblocks, int blk, int hd) {
-    return align256(64 * sizeof(int)) + align256(dq_max_items(nblocks) * sizeof(int4)) +
-           align256(nblocks * sizeof(int2)) + align256(nblocks * sizeof(int)) +
-           align256(kDqChunkBelow * sizeof(int)) + (size_t)kDqMaxSlots * blk * hd * sizeof(float);
-}
-
-__host__ __device__ inline DqWorkspace dq_workspace(void* base, size_t nblocks, int blk, int hd) {
-    char* p = static_cast<char*>(base);
-    DqWorkspace w;
-    w.ctrl = reinterpret_cast<int*>(p);
-    p += align256(64 * sizeof(int));
-    w.items = reinterpret_cast<int4*>(p);
-    p += align256(dq_max_items(nblocks) * sizeof(int4));
-    w.blk = reinterpret_cast<int2*>(p);
-    p += align256(nblocks * sizeof(int2));
-    w.skip = reinterpret_cast<int*>(p);
-    p += align256(nblocks * sizeof(int));
-    w.chunked = reinterpret_cast<int*>(p);
-    p += align256(kDqChunkBelow * sizeof(int));
-    w.part = reinterpret_cast<float*>(p);
-    (void)blk;
-    (void)hd;
-    return w;
-}
-
-// Block-wide exclusive scans of M ints per thread (1024 threads) at once:
-// x[m] becomes its exclusive prefix and total[m] the sum.  `sh` holds
-// 17 M ints.
-template <int M>
-__device__ __forceinline__ void block_scan_1024(int (&x)[M], int* sh, int (&total)[M]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) inc[m] = x[m];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const int y = __shfl_up(inc[m], off);
-            if (lane >= off) inc[m] += y;
-        }
-    if (lane == 63)
-#pragma unroll
-        for (int m = 0; m < M; ++m) sh[17 * m + wave] = inc[m];
-    __syncthreads();
-    if (threadIdx.x < M) {
-        int* q = sh + 17 * threadIdx.x;
-        int run = 0;
-        for (int w = 0; w < 16; ++w) {
-            const int t = q[w];
-            q[w] = run;
-            run += t;
-        }
-        q[16] = run;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        total[m] = sh[17 * m + 16];
-        x[m] = sh[17 * m + wave] + inc[m] - x[m];
-    }
-    __syncthreads();
-}
-
-// One workgroup of 1024 threads.  Entries e = 0 .. E-1 run over (block i
-// descending, head bh ascending); an entry is kept when its block weight is
-// non-zero.  Emits the items in that order and the per-block slot table.
-// Chunk lengths never exceed this many key steps: chunking happens with fewer
-// than kDqChunkBelow kept blocks of at most 8192 steps, cut into T / kDqChunkItems
-// step pieces or longer.
-constexpr int kDqMaxChunk = ((kDqChunkBelow - 1) * 8192 + kDqChunkItems - 1) / kDqChunkItems;
-
-constexpr int kDqPlanLds = 16384;  // block weights the plan stages in LDS (64 KiB)
-template <int BLK>
-__global__ __launch_bounds__(1024) void dq_plan_kernel(const float* __restrict__ block_w, int BHq,
-                                                       int nqb, int N, int causal, DqWorkspace ws) {
-    __shared__ int sh[17 * 3];
-    __shared__ int bucket[kDqMaxChunk + 1];  // chunk count, then next queue position, per length
-    __shared__ float sw[kDqPlanLds];
-    const int E = BHq * nqb;
-    const int tid = threadIdx.x;
-    // the passes below visit the weights in a strided order, four times: read
-    // them once, coalesced, into LDS when they fit
-    const bool staged = E <= kDqPlanLds;
-    if (staged) {
-        for (int x = 4 * tid; x < E; x += 4 * 1024) {
-            if (x + 4 <= E && (E & 3) == 0) {
-                *reinterpret_cast<f32x4*>(&sw[x]) = *reinterpret_cast<const f32x4*>(&block_w[x]);
-            } else {
-                for (int y = x; y < min(E, x + 4); ++y) sw[y] = block_w[y];
-            }
-        }
-        __syncthreads();
-    }
-    // one copy of the plan per source of the weights, so each reads its own
-    // address space (a choice between the two would read through flat loads)
-    auto plan = [&](auto weight) __attribute__((always_inline)) {
-        const int per = (E + 1023) / 1024;
-        const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-        const int nks = (N + kQN - 1) / kQN;  // key steps of a head (the last may be partial)
-        auto steps = [&](int i) { return causal ? min((i * BLK + BLK - 1) / kQN + 1, nks) : nks; };
-        auto entry = [&](int e, int& bh, int& i) {
-            i = nqb - 1 - e / BHq;
-            bh = e % BHq;
-        };
-        // pass 1: kept blocks K and their total key steps T
-        int kc = 0, ts = 0;
-        for (int e = e0; e < e1; ++e) {
-            int bh, i;
-            entry(e, bh, i);
-            if (weight(bh * nqb + i) != 0.f) {
-                ++kc;
-                ts += steps(i);
-            }
-        }
-        int kt2[2] = {kc, ts}, tot2[2];
-        block_scan_1024(kt2, sh, tot2);
-        const int kpre = kt2[0], K = tot2[0], T = tot2[1];
-        const bool chunking = K < kDqChunkBelow;
-        const int CL = chunking ? max(kDqMinChunk, (T + kDqChunkItems - 1) / kDqChunkItems) : (1 << 30);
-        // pass 2: compute items, partial slots and chunked blocks per thread
-        int ni = 0, nsl = 0, nck = 0;
-        for (int e = e0; e < e1; ++e) {
-            int bh, i;
-            entry(e, bh, i);
-            if (weight(bh * nqb + i) != 0.f) {
-                const int nch = (steps(i) + CL - 1) / CL;
-                ni += nch;
-                nsl += nch > 1 ? nch : 0;
-                nck += nch > 1;
-            }
-        }
-        int isc[3] = {ni, nsl, nck}, itot[3];
-        block_scan_1024(isc, sh, itot);
-        int it = isc[0], sl = isc[1], ck = isc[2];
-        const int n_items = itot[0], n_chunked = itot[2];
-        if (chunking) {
-            // Queue order longest first over all chunks (not block by block): a
-            // counting sort by chunk length, so short remainders end the queue.
-            for (int c = tid; c <= CL; c += 1024) bucket[c] = 0;
-            __syncthreads();
-            for (int e = e0; e < e1; ++e) {
-                int bh, i;
-                entry(e, bh, i);
-                if (weight(bh * nqb + i) != 0.f) {
-                    const int L = steps(i);
-                    const int nch = (L + CL - 1) / CL;
-                    for (int c = 0; c < nch; ++c)
-                        atomicAdd(&bucket[((c + 1) * L) / nch - (c * L) / nch], 1);
-                }
-            }
-            __syncthreads();
-            // exclusive prefix over lengths, longest first: bucket[len] = first
-            // queue position of its chunks
-            constexpr int PER = (kDqMaxChunk + 1 + 1023) / 1024;
-            int cnt[PER], tot = 0;
-    #pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int len = CL - (tid * PER + u);
-                cnt[u] = len >= 1 ? bucket[len] : 0;
-                tot += cnt[u];
-            }
-            int run1[1] = {tot}, all[1];
-            block_scan_1024(run1, sh, all);
-            int run = run1[0];
-    #pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int len = CL - (tid * PER + u);
-                if (len >= 1) bucket[len] = run;
-                run += cnt[u];
-            }
-            __syncthreads();
-        }
-        int sk = e0 - kpre;  // skipped blocks before this thread's entries
-        for (int e = e0; e < e1; ++e) {
-            int bh, i;
-            entry(e, bh, i);
-            const int blk = bh * nqb + i;
-            int2 info = make_int2(-1, 0);
-            if (weight(blk) != 0.f) {
-                const int L = steps(i);
-                const int nch = (L + CL - 1) / CL;
-                info = make_int2(nch > 1 ? sl : -1, nch);
-                for (int c = 0; c < nch; ++c) {
-                    // equal chunks (lengths differ by at most one step)
-                    const int s0 = (c * L) / nch, s1 = ((c + 1) * L) / nch;
-                    const int at = chunking ? atomicAdd(&bucket[s1 - s0], 1) : it++;
-                    ws.items[at] = make_int4(bh, i, s0 | (s1 << 16), nch > 1 ? sl + c : -1);
-                }
-                if (nch > 1) {
-                    sl += nch;
-                    ws.chunked[ck++] = blk;
-                }
-            } else {
-                ws.skip[sk++] = blk;
-            }
-            ws.blk[blk] = info;
-        }
-        // zero-fill items go last: they take up the walk's tail
-        const int n_skip = E - K;
-        const int n_zero = (n_skip + kDqZeroPer - 1) / kDqZeroPer;
-        for (int z = tid; z < n_zero; z += 1024)
-            ws.items[n_items + z] =
-                make_int4(-1, z * kDqZeroPer, min(kDqZeroPer, n_skip - z * kDqZeroPer), 0);
-        if (tid == 0) {
-            ws.ctrl[0] = n_items + n_zero;
-            ws.ctrl[1] = 0;
-            ws.ctrl[2] = n_chunked;
-        }
-    };
-    if (staged) plan([&](int blk) { return sw[blk]; });
-    else plan([&](int blk) { return block_w[blk]; });
-}
-
-// Persistent dQ walk.  Each item is one kept block's key steps [s0, s1).  A
-// workgroup has 4 waves of 32 query rows: for 128-row blocks one stream of 4
-// waves takes every step (two workgroups per CU); for 64-row blocks two
-// streams of 2 waves split the steps, even to stream 0 and odd to stream 1,
-// and add their partials in LDS at the end.  The result goes to the dq rows
-// (single-chunk block) or to the item's fp32 partial slot.  Each stream
-// double-buffers its K/V tiles in two LDS arrays of its own, and the code of
-// each stream and buffer names its arrays at compile time: loads to LDS into
-// one array then never hold back the LDS reads of another (the compiler waits
-// for a load to LDS before reading the same array).  The next step's loads go
-// out among the current step's score MFMAs.  Steps run without branches: keys
-// the causal mask hides, and a stream's missing last step, add exact zeros.
 template <int BLK>
 struct DqShape {
     static constexpr int NS = BLK >= 128 ? 1 : 2;  // streams per workgroup
@@ -1146,14 +1171,24 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     const DqWorkspace ws = dq_workspace(workspace, nblocks, pb.block, pb.d);
 #define LF_BWD(DD, BB, CC)                                                                      \
     if (pb.d == DD && pb.block == BB && (pb.causal != 0) == CC) {                               \
-        if (do_kv)                                                                              \
-            hipLaunchKernelGGL((dkdv_bf16_kernel<DD, BB, CC>), dim3(nwg_kv), dim3(512), 0, st, \
-                               (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
+        /* with both phases, the plan rides along in the dK/dV launch where it fits */          \
+        constexpr bool fuse_ok = kBM * DD * sizeof(bf16) >= kDqBucketInts * sizeof(int);        \
+        const bool fused = fuse_ok && do_kv && do_q;                                            \
+        if (do_kv && fused)                                                                     \
+            hipLaunchKernelGGL((dkdv_bf16_kernel<DD, BB, CC, fuse_ok>), dim3(nwg_kv + 1),        \
+                               dim3(512), 0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, \
+                               lse, (const bf16*)dout, D, kept_idx, kept_count, block_w,        \
+                               (bf16*)dk, (bf16*)dv, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb,         \
+                               pb.scale, sl2, ws);                                              \
+        else if (do_kv)                                                                         \
+            hipLaunchKernelGGL((dkdv_bf16_kernel<DD, BB, CC, false>), dim3(nwg_kv), dim3(512),  \
+                               0, st, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,      \
                                (const bf16*)dout, D, kept_idx, kept_count, block_w, (bf16*)dk,  \
-                               (bf16*)dv, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale, sl2);    \
+                               (bf16*)dv, pb.B, pb.Hq, pb.Hkv, pb.N, pb.nqb, pb.scale, sl2, ws); \
         if (do_q) {                                                                             \
-            hipLaunchKernelGGL((dq_plan_kernel<BB>), dim3(1), dim3(1024), 0, st, block_w,       \
-                               pb.B * pb.Hq, pb.nqb, pb.N, pb.causal, ws);                      \
+            if (!fused)                                                                         \
+                hipLaunchKernelGGL((dq_plan_kernel<BB>), dim3(1), dim3(1024), 0, st, block_w,   \
+                                   pb.B * pb.Hq, pb.nqb, pb.N, pb.causal, ws);                  \
             hipLaunchKernelGGL((dq_bf16_kernel<DD, BB, CC>),                                     \
                                dim3(kDqGrid * DqShape<BB>::PER_CU), dim3(DqShape<BB>::NT), 0, st, \
                                (const bf16*)q, (const bf16*)k, (const bf16*)v, lse,             \
