@@ -1,6 +1,7 @@
 """GPU invariants of the path (through the C ABI): determinism, never-loaded
-skipped tiles (NaN poisoning), nesting across budgets, degenerate heads,
-independence of the backward's two phases."""
+skipped tiles (NaN poisoning), outputs fully written (NaN-filled buffers),
+nesting across budgets, degenerate heads, independence of the backward's two
+phases."""
 import math
 
 import numpy as np
@@ -16,6 +17,8 @@ pytestmark = pytest.mark.gpu
 
 CFG = Config("inv", 1, 8, 2, 1024, 128, "bf16", True, 128, 2.0, boost_frac=0.125, boost=20.0)
 CFG64 = Config("inv64", 2, 4, 4, 640, 64, "bf16", False, 64, 1.5)
+CFGR = Config("inv_ragged", 1, 8, 2, 1000, 128, "bf16", True, 128, 2.0, boost_frac=0.125,
+              boost=20.0)
 
 
 def _bits(t):
@@ -55,6 +58,32 @@ def test_skipped_blocks_are_never_read(cfg):
     torch.cuda.synchronize()
     for name, x in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert np.array_equal(_bits(x), _bits(g[name])), name
+
+
+@pytest.mark.parametrize("cfg", [CFG, CFG64, CFGR], ids=["causal_d128", "noncausal_d64", "ragged"])
+@pytest.mark.parametrize("apart", [False, True], ids=["one_call", "phases_apart"])
+def test_outputs_fully_written(cfg, apart):
+    # dQ, dK, dV start as NaN: every element must be written, the rows of
+    # skipped blocks as exact zeros, whichever kernel writes them (the dK/dV
+    # walk in one call, the dQ walk when the phases run apart)
+    inp = make_inputs(cfg, 0)
+    g = run_gpu(cfg, inp, 0.2, seed=1)
+    keep = g["sel"]["block_w"] != 0
+    assert 0 < int(keep.sum()) < keep.numel()
+    outs = tuple(torch.full_like(g[n], float("nan")) for n in ("dq", "dk", "dv"))
+    kw = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=outs)
+    args = (g["q"], g["k"], g["v"], g["lse"], g["dout"], g["sel"])
+    if apart:
+        bd.attn_bwd(*args, phases=bd.BWD_DQ, **kw)
+        bd.attn_bwd(*args, phases=bd.BWD_DKDV, **kw)
+    else:
+        bd.attn_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for name, x in zip(("dq", "dk", "dv"), outs):
+        assert not torch.isnan(x).any(), name
+        assert np.array_equal(_bits(x), _bits(g[name])), name
+    rows = keep.repeat_interleave(cfg.block, dim=2)[:, :, :cfg.N]
+    assert int((outs[0][~rows] != 0).sum()) == 0
 
 
 def test_kept_sets_nest_across_budgets():
