@@ -230,10 +230,13 @@ def main():
     others = dict(
         fwd=dict(bound="mfma", achieved=round(F_fwd / (t_fwd * 1e-3) / 1e12, 2), peak=peak,
                  unit="TFLOP/s"),
-        select_mass_pass=dict(bound="hbm", bytes_per_launch=2 * q.numel() * q.element_size(),
+        select_mass_pass=dict(bound="hbm",
+                              bytes_per_launch=int(q.numel() * q.element_size() * (1.0 + 2.0 * float(kept.mean()))
+                                                   + 4 * cfg.B * cfg.Hq * cfg.N),
                               unit="GB/s", peak=8000.0,
-                              note="select = streaming pass (dO, O read) + per-head tau kernel; "
-                                   "time includes both"),
+                              note="select = mass pass (dO read once) + per-head tau kernel + D "
+                                   "pass (dO, O of kept blocks read, D written); time includes "
+                                   "all three"),
     )
     others["select_mass_pass"]["achieved_incl_tau"] = round(
         others["select_mass_pass"]["bytes_per_launch"] / (t_sel * 1e-3) / 1e9, 1)

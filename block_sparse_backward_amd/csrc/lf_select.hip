@@ -1,6 +1,7 @@
-// Block selection: per-block gradient masses and the D row term (one HBM
-// streaming pass), then per (batch, head) the budget threshold tau, the Philox
-// draw, the 1/p weights and the compacted kept-block list.
+// Block selection: per-block gradient masses (one HBM streaming pass over
+// dO), then per (batch, head) the budget threshold tau, the Philox draw, the
+// 1/p weights and the compacted kept-block list, then the D row term of the
+// kept blocks only (the backward reads no other row's D).
 //
 // Method: the LazyFlash journal entry on gyom.fr ("LazyFlash allège la
 // rétropropagation de l'attention, 5,72 fois"), section "Un budget sur la masse
@@ -19,10 +20,10 @@
 namespace lf {
 
 // ---------------------------------------------------------------------------
-// Kernel A: one workgroup of 256 threads per query block (b, h, i).
+// Kernel A: one workgroup of 256 threads per query block (b, h, i): its mass.
 // The block is the run of L = block*d elements at row i*block of head (b, h);
 // when N is not a multiple of block the last block's missing rows read as
-// zeros (they add exact zeros to the mass) and get no D.
+// zeros (they add exact zeros to the mass).
 // Thread t owns elements e + 8t + 2048s (e < 8, s < L/2048), loaded as one
 // 16-byte vector per s (coalesced), which lets the fp64 halving tree run as:
 // in-thread levels over s, then 8 cross-thread levels (t + 128, t + 64, ...,
@@ -52,47 +53,24 @@ __device__ __forceinline__ void load8_buf(__amdgpu_buffer_rsrc_t rs, int voff, i
 }
 
 template <typename T, int L, int HD>
-__global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
-                                                     const T* __restrict__ dout,
-                                                     float* __restrict__ D,
-                                                     double* __restrict__ mass, int N, int nqb) {
+__global__ __launch_bounds__(256) void mass_kernel(const T* __restrict__ dout,
+                                                   double* __restrict__ mass, int N, int nqb) {
     constexpr int S = L / 2048;
-    constexpr int LANES_PER_ROW = HD / 8;
     constexpr int ROWS = L / HD;  // = block
     const size_t blk = blockIdx.x;
     const size_t bh = blk / (size_t)nqb;
     const int row0 = (int)(blk % (size_t)nqb) * ROWS;
-    const int nrows = min(ROWS, N - row0);  // rows of this block that exist
     const int t = threadIdx.x;
     // buffer loads over the head: rows past N read as zeros, with no branch
-    const size_t head = bh * (size_t)N * HD;
     const uint32_t head_bytes = (uint32_t)((size_t)N * HD * sizeof(T));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dout + head, head_bytes);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dout + bh * (size_t)N * HD, head_bytes);
     const int off0 = row0 * HD * (int)sizeof(T);  // the block's first row in the head
 
     float x[S][8];
-    float y[S][8];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int vo = (8 * t + 2048 * s) * (int)sizeof(T);
-        load8_buf<T>(rg, vo, off0, x[s]);
-        load8_buf<T>(ro, vo, off0, y[s]);
-    }
+    for (int s = 0; s < S; ++s) load8_buf<T>(rg, (8 * t + 2048 * s) * (int)sizeof(T), off0, x[s]);
 
-    // D: each (t, s) covers 8 columns of row (8t + 2048s) / HD.
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part += x[s][e] * y[s][e];
-#pragma unroll
-        for (int off = LANES_PER_ROW / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        const int r = (8 * t + 2048 * s) / HD;
-        if ((t % LANES_PER_ROW) == 0 && r < nrows) D[bh * (size_t)N + row0 + r] = part;
-    }
-
-    // Mass: squares are exact in fp64; only the additions round.
+    // squares are exact in fp64; only the additions round
     double v[S][8];
 #pragma unroll
     for (int s = 0; s < S; ++s)
@@ -132,6 +110,54 @@ __global__ __launch_bounds__(256) void mass_d_kernel(const T* __restrict__ o,
             for (int e = 0; e < 2; ++e) w[e] = __dadd_rn(w[e], w[e + 2]);
             mass[blk] = __dadd_rn(w[0], w[1]);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel C: D = rowsum(dO * O) for the rows of kept blocks, one workgroup per
+// query block (the same thread mapping as kernel A: each (t, s) covers 8
+// columns of row (8t + 2048s) / HD); a skipped block's rows get D = 0, which
+// the backward never reads (it loads nothing of a skipped block).
+// ---------------------------------------------------------------------------
+template <typename T, int L, int HD>
+__global__ __launch_bounds__(256) void d_kept_kernel(const T* __restrict__ o,
+                                                     const T* __restrict__ dout,
+                                                     const float* __restrict__ block_w,
+                                                     float* __restrict__ D, int N, int nqb) {
+    constexpr int S = L / 2048;
+    constexpr int LANES_PER_ROW = HD / 8;
+    constexpr int ROWS = L / HD;
+    const size_t blk = blockIdx.x;
+    const size_t bh = blk / (size_t)nqb;
+    const int row0 = (int)(blk % (size_t)nqb) * ROWS;
+    const int nrows = min(ROWS, N - row0);  // rows of this block that exist
+    const int t = threadIdx.x;
+    float* Dr = D + bh * (size_t)N + row0;
+    if (block_w[blk] == 0.f) {
+        for (int r = t; r < nrows; r += 256) Dr[r] = 0.f;
+        return;
+    }
+    const uint32_t head_bytes = (uint32_t)((size_t)N * HD * sizeof(T));
+    const size_t head = bh * (size_t)N * HD;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(dout + head, head_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + head, head_bytes);
+    const int off0 = row0 * HD * (int)sizeof(T);
+    float x[S][8], y[S][8];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int vo = (8 * t + 2048 * s) * (int)sizeof(T);
+        load8_buf<T>(rg, vo, off0, x[s]);
+        load8_buf<T>(ro, vo, off0, y[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += x[s][e] * y[s][e];
+#pragma unroll
+        for (int off = LANES_PER_ROW / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        const int r = (8 * t + 2048 * s) / HD;
+        if ((t % LANES_PER_ROW) == 0 && r < nrows) Dr[r] = part;
     }
 }
 
@@ -403,16 +429,14 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
 
 // ---------------------------------------------------------------------------
 template <typename T>
-static hipError_t launch_mass(const Problem& pb, const void* o, const void* dout, float* D,
-                              double* mass, hipStream_t st) {
+static hipError_t launch_mass(const Problem& pb, const void* dout, double* mass, hipStream_t st) {
     const unsigned nblk = (unsigned)((size_t)pb.B * pb.Hq * pb.nqb);
     const int L = pb.block * pb.d;
-    const T* po = static_cast<const T*>(o);
     const T* pd = static_cast<const T*>(dout);
 #define LF_MASS(LL, DD)                                                                     \
     if (L == LL && pb.d == DD) {                                                            \
-        hipLaunchKernelGGL((mass_d_kernel<T, LL, DD>), dim3(nblk), dim3(256), 0, st, po, pd, \
-                           D, mass, pb.N, pb.nqb);                                          \
+        hipLaunchKernelGGL((mass_kernel<T, LL, DD>), dim3(nblk), dim3(256), 0, st, pd, mass, \
+                           pb.N, pb.nqb);                                                   \
         return hipGetLastError();                                                           \
     }
     LF_MASS(4096, 64)
@@ -420,6 +444,27 @@ static hipError_t launch_mass(const Problem& pb, const void* o, const void* dout
     LF_MASS(8192, 128)
     LF_MASS(16384, 128)
 #undef LF_MASS
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_d_kept(const Problem& pb, const void* o, const void* dout,
+                               const float* block_w, float* D, hipStream_t st) {
+    const unsigned nblk = (unsigned)((size_t)pb.B * pb.Hq * pb.nqb);
+    const int L = pb.block * pb.d;
+    const T* po = static_cast<const T*>(o);
+    const T* pd = static_cast<const T*>(dout);
+#define LF_DK(LL, DD)                                                                        \
+    if (L == LL && pb.d == DD) {                                                             \
+        hipLaunchKernelGGL((d_kept_kernel<T, LL, DD>), dim3(nblk), dim3(256), 0, st, po, pd,  \
+                           block_w, D, pb.N, pb.nqb);                                        \
+        return hipGetLastError();                                                            \
+    }
+    LF_DK(4096, 64)
+    LF_DK(8192, 64)
+    LF_DK(8192, 128)
+    LF_DK(16384, 128)
+#undef LF_DK
     return hipErrorInvalidValue;
 }
 
@@ -441,8 +486,8 @@ hipError_t launch_empty_heads(double* tau, int32_t* kept_count, int n, hipStream
 hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int rule,
                          double param, uint64_t seed, float* D, double* mass, double* tau,
                          float* block_w, int32_t* kept_idx, int32_t* kept_count, hipStream_t st) {
-    hipError_t e = pb.bf16 ? launch_mass<bf16>(pb, o, dout, D, mass, st)
-                           : launch_mass<float>(pb, o, dout, D, mass, st);
+    hipError_t e = pb.bf16 ? launch_mass<bf16>(pb, dout, mass, st)
+                           : launch_mass<float>(pb, dout, mass, st);
     if (e != hipSuccess) return e;
     int P = 1;
     while (P < pb.nqb) P <<= 1;
@@ -455,7 +500,10 @@ hipError_t launch_select(const Problem& pb, const void* o, const void* dout, int
     hipLaunchKernelGGL(tau_select_kernel, dim3((unsigned)(pb.B * pb.Hq)), dim3(kSelThreads), lds,
                        st, mass, rule, param, seed, pb.b0, pb.Hq, pb.nqb, P, tau, block_w,
                        kept_idx, kept_count);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return pb.bf16 ? launch_d_kept<bf16>(pb, o, dout, block_w, D, st)
+                   : launch_d_kept<float>(pb, o, dout, block_w, D, st);
 }
 
 }  // namespace lf

@@ -102,7 +102,11 @@ lf_status lf_attn_fwd(const lf_shape* shape, const void* q, const void* k, const
  * gradient non biaisé" of the LazyFlash entry; the rule is stated above.
  *   o, dout [B,Hq,N,d] (dtype)                         in
  *   delta in [0, 1), seed                              in
- *   D [B,Hq,N] float32                                 out: rowsum(dout * o)
+ *   D [B,Hq,N] float32                                 out: rowsum(dout * o) on the
+ *                                                           rows of kept blocks, 0 on
+ *                                                           the rows of skipped blocks
+ *                                                           (the backward reads only
+ *                                                           kept rows' D)
  *   mass [B,Hq,nqb] float64                            out: block masses (bit-exact)
  *   tau [B,Hq] float64                                 out: per-head threshold
  *   block_w [B,Hq,nqb] float32                         out: 1/p if kept, else 0

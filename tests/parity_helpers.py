@@ -78,7 +78,9 @@ def check_fwd_rows(cfg, inp, gpu, heads, rows):
 
 
 def check_d_rows(cfg, inp, gpu, heads, rows):
-    """D = rowsum(dO * O) from the select kernel, vs the oracle's exact O.
+    """D = rowsum(dO * O) from the select pass, vs the oracle's exact O, on the
+    sampled rows that lie in kept blocks (the pass writes D only there); the
+    sampled rows of skipped blocks must hold exact zeros.
 
     Returns the largest ratio of each row's error to its allowed error: the
     output tolerance (relative to the largest |D| of the sample) plus the
@@ -88,15 +90,25 @@ def check_d_rows(cfg, inp, gpu, heads, rows):
     A value <= 1 passes."""
     q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
     G = cfg.Hq // cfg.Hkv
+    rows = np.asarray(rows)
+    keep = gpu["sel"]["block_w"].cpu().numpy() != 0
     got, want, floor = [], [], []
     ulp = 2.0 ** -8 if cfg.dtype == "bf16" else 2.0 ** -23
     for b, h in heads:
+        kr = keep[b, h, rows // cfg.block]
+        d_rows = host(gpu["sel"]["D"][b, h, rows])
+        assert np.all(d_rows[~kr] == 0.0), "D of a skipped block's row is not zero"
+        if not kr.any():
+            continue
+        r = rows[kr]
         o_r, _ = oracle.attn_fwd_rows(q64[b, h], k64[b, h // G], v64[b, h // G], cfg.scale,
-                                      cfg.causal, rows)
-        want.append((d64[b, h, rows] * o_r).sum(axis=1))
-        floor.append(ulp * (np.abs(d64[b, h, rows]) * np.abs(o_r)).sum(axis=1))
-        got.append(host(gpu["sel"]["D"][b, h, rows]))
-    got, want, floor = np.stack(got), np.stack(want), np.stack(floor)
+                                      cfg.causal, r)
+        want.append((d64[b, h, r] * o_r).sum(axis=1))
+        floor.append(ulp * (np.abs(d64[b, h, r]) * np.abs(o_r)).sum(axis=1))
+        got.append(d_rows[kr])
+    if not got:
+        return 0.0
+    got, want, floor = np.concatenate(got), np.concatenate(want), np.concatenate(floor)
     allowed = TOL[cfg.dtype] * np.abs(want).max() + floor
     return float((np.abs(got - want) / allowed).max())
 
