@@ -17,7 +17,7 @@ __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block
            "attn_bwd_varlen", "varlen_block_offsets"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
 EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_block_select_rule", "lf_attn_bwd",

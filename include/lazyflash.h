@@ -254,7 +254,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 5
+#define LF_ABI_VERSION 6  /* 6: D is written on the rows of kept blocks only */
 
 #ifdef __cplusplus
 }
