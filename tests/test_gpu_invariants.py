@@ -19,6 +19,8 @@ CFG = Config("inv", 1, 8, 2, 1024, 128, "bf16", True, 128, 2.0, boost_frac=0.125
 CFG64 = Config("inv64", 2, 4, 4, 640, 64, "bf16", False, 64, 1.5)
 CFGR = Config("inv_ragged", 1, 8, 2, 1000, 128, "bf16", True, 128, 2.0, boost_frac=0.125,
               boost=20.0)
+CFGB64 = Config("inv_d128_b64", 1, 4, 2, 704, 128, "bf16", True, 64, 2.0, boost_frac=0.125,
+                boost=20.0)
 
 
 def _bits(t):
@@ -60,7 +62,8 @@ def test_skipped_blocks_are_never_read(cfg):
         assert np.array_equal(_bits(x), _bits(g[name])), name
 
 
-@pytest.mark.parametrize("cfg", [CFG, CFG64, CFGR], ids=["causal_d128", "noncausal_d64", "ragged"])
+@pytest.mark.parametrize("cfg", [CFG, CFG64, CFGR, CFGB64],
+                         ids=["causal_d128", "noncausal_d64", "ragged", "d128_b64"])
 @pytest.mark.parametrize("apart", [False, True], ids=["one_call", "phases_apart"])
 def test_outputs_fully_written(cfg, apart):
     # dQ, dK, dV start as NaN: every element must be written, the rows of
@@ -122,8 +125,11 @@ def test_nonfinite_and_zero_heads():
     assert not torch.isfinite(g["dq"][0, 1]).all()
 
 
-def test_phases_are_independent():
-    cfg = CFG64
+@pytest.mark.parametrize("cfg", [CFG64, CFG, CFGB64], ids=["noncausal_d64", "causal_d128",
+                                                          "d128_b64"])
+def test_phases_are_independent(cfg):
+    # the one call (where d = 128 runs the dQ plan inside the dK/dV launch)
+    # and the two phases in reverse order give the same bits
     inp = make_inputs(cfg, 0)
     g = run_gpu(cfg, inp, 0.1, seed=5)
     dq = torch.full_like(g["dq"], 7.0)
