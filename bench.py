@@ -63,7 +63,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the method needs no exchange "
+        print("bench.py: measures one GPU only (the method needs no exchange "
               "between GPUs inside the attention backward); run it with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
