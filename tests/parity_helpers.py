@@ -23,14 +23,16 @@ def max_abs_rel(x, ref):
     return float(num / den)
 
 
-def run_gpu(cfg, inp, delta, seed, device="cuda:0"):
-    """fwd -> select -> bwd on the GPU; returns (device tensors dict)."""
+def run_gpu(cfg, inp, delta, seed, device="cuda:0", scale=None):
+    """fwd -> select -> bwd on the GPU (softmax scale cfg.scale unless given);
+    returns (device tensors dict)."""
+    scale = cfg.scale if scale is None else scale
     q, k, v, do = (inp[n].to(device) for n in ("q", "k", "v", "dout"))
-    o, lse = bd.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, block=cfg.block)
+    o, lse = bd.attn_fwd(q, k, v, causal=cfg.causal, scale=scale, block=cfg.block)
     sel = bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
-                          scale=cfg.scale, heads_kv=cfg.Hkv)
+                          scale=scale, heads_kv=cfg.Hkv)
     dq, dk, dv = bd.attn_bwd(q, k, v, lse, do, sel, block=cfg.block, causal=cfg.causal,
-                             scale=cfg.scale)
+                             scale=scale)
     torch.cuda.synchronize(device)
     return dict(q=q, k=k, v=v, dout=do, o=o, lse=lse, sel=sel, dq=dq, dk=dk, dv=dv)
 

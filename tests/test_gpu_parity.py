@@ -38,6 +38,14 @@ SMALL = {
     "bf16_ragged_N333_noncausal_d128_b64": (Config("r4", 1, 2, 2, 333, 128, "bf16", False, 64, 0.5),
                                             0.0),
     "f32_ragged_N300": (Config("r5", 1, 2, 2, 300, 64, "f32", True, 64, 1.0), 0.1),
+    # fewer rows than one sub-tile: one partial block, one partial key tile
+    "bf16_N50_causal_d128_b128": (Config("e1", 1, 4, 2, 50, 128, "bf16", True, 128, 1.5), 0.1),
+    "bf16_N1_causal_d64_b64": (Config("e2", 2, 2, 1, 1, 64, "bf16", True, 64, 1.0), 0.0),
+    # batch x kv heads a multiple of 8: the workgroup-to-XCD mappings of the
+    # forward and the dK/dV walk take their rotated path (B > 1 included)
+    "bf16_xcd_B2_Hkv4": (Config("x1", 2, 8, 4, 640, 128, "bf16", True, 128, 2.0,
+                                boost_frac=0.1, boost=20.0), 0.1),
+    "bf16_xcd_B3_Hkv8_d64_b64": (Config("x2", 3, 8, 8, 384, 64, "bf16", True, 64, 1.5), 0.1),
 }
 
 
@@ -69,6 +77,36 @@ def test_small_full_parity(name):
     # rows of skipped blocks of dq are exact zeros
     skipped = np.repeat(~ref_sel["keep"], cfg.block, axis=2)[:, :, :cfg.N]
     assert np.all(host(gpu["dq"])[skipped] == 0.0)
+
+
+# Softmax scales other than 1/sqrt(d): a negative scale (the forward negates Q
+# so that the running max is taken over the scaled scores), a small one and a
+# sharp one; the selection does not depend on the scale, D and the gradients do.
+SCALES = {
+    "bf16_causal_d128_neg": (Config("c1", 1, 4, 2, 384, 128, "bf16", True, 128, 1.5), -0.09, 0.1),
+    "bf16_noncausal_d64_small": (Config("c2", 2, 2, 2, 256, 64, "bf16", False, 64, 1.0), 0.03, 0.2),
+    "bf16_causal_d64_b128_sharp": (Config("c3", 1, 4, 1, 320, 64, "bf16", True, 128, 1.0), 0.5, 0.1),
+    "f32_causal_d64_neg": (Config("c4", 1, 2, 1, 192, 64, "f32", True, 64, 1.0), -0.2, 0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(SCALES))
+def test_softmax_scale_parity(name):
+    cfg, scale, delta = SCALES[name]
+    print(f"[parity-scale] {name} {cfg} scale={scale} delta={delta}", flush=True)
+    inp = make_inputs(cfg, 3)
+    gpu = run_gpu(cfg, inp, delta, seed=5, scale=scale)
+    ref_sel = check_select_exact(cfg, inp, gpu, delta, 5)
+    q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
+    o_ref, lse_ref = oracle.attn_fwd(q64, k64, v64, scale, cfg.causal)
+    tol = TOL[cfg.dtype]
+    assert max_abs_rel(host(gpu["o"]), o_ref) <= tol
+    assert np.abs(host(gpu["lse"]) - lse_ref).max() <= LSE_TOL[cfg.dtype]
+    dq, dk, dv = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, ref_sel["keep"],
+                                        ref_sel["w"], scale, cfg.causal)
+    errs = [max_abs_rel(host(gpu[n]), r) for n, r in (("dq", dq), ("dk", dk), ("dv", dv))]
+    print(f"[parity-scale] {name} kept={ref_sel['keep'].mean():.3f} errs={errs}", flush=True)
+    assert max(errs) <= tol, errs
 
 
 _CACHE = {}
