@@ -202,6 +202,33 @@ __device__ __forceinline__ uint64_t philox_first_word(uint64_t c0, uint64_t c1, 
 constexpr int kSelThreads = 1024;
 constexpr int kRuleBudget = 0, kRuleFraction = 1, kRuleTopk = 2;
 
+// Running sums dst[k] = fl(dst[k - 1] + src[k]) for k < n, in ascending order
+// (one rounding per addition), by one thread; the loads run one batch ahead
+// of the dependent additions.  src and dst may be the same array.
+__device__ __forceinline__ void running_sum(const double* src, double* dst, int n) {
+    constexpr int NB = 16;
+    double acc = 0.0, cur[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) cur[u] = src[min(u, n - 1)];
+    int k0 = 0;
+    for (; k0 + NB <= n; k0 += NB) {  // whole batches: no branch among the additions
+        double nxt[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) nxt[u] = src[min(k0 + NB + u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            acc = __dadd_rn(acc, cur[u]);
+            dst[k0 + u] = acc;
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) cur[u] = nxt[u];
+    }
+    for (int u = 0; k0 + u < n; ++u) {  // the last, partial batch
+        acc = __dadd_rn(acc, src[k0 + u]);
+        dst[k0 + u] = acc;
+    }
+}
+
 __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
     const double* __restrict__ mass, int rule, double param, uint64_t seed, int b0, int Hq,
     int nqb, int P, double* __restrict__ tau_out, float* __restrict__ block_w,
@@ -287,30 +314,13 @@ __global__ __launch_bounds__(kSelThreads) void tau_select_kernel(
     if (need_sort && rule == kRuleTopk) {
         if (tid == 0) s_tau = srt[n - topk];  // the k-th largest positive mass
     } else if (need_sort) {
-        // sequential running sums in ascending order (one rounding per op)
-        if (tid == 0) {
-            double a = 0.0, q = 0.0;
-            int k = 0;
-            for (; k + 8 <= n; k += 8) {  // the next 8 masses read ahead of the chain
-                double mk[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) mk[u] = srt[k + u];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    a = __dadd_rn(a, mk[u]);
-                    q = __dadd_rn(q, __dmul_rn(mk[u], mk[u]));
-                    accA[k + u] = a;
-                    accQ[k + u] = q;
-                }
-            }
-            for (; k < n; ++k) {
-                const double mk = srt[k];
-                a = __dadd_rn(a, mk);
-                q = __dadd_rn(q, __dmul_rn(mk, mk));
-                accA[k] = a;
-                accQ[k] = q;
-            }
-        }
+        // running sums in ascending order, each addition rounded in turn:
+        // A over the masses (wave 0) and Q over their squares (wave 1, the
+        // squares formed first by all threads) run side by side
+        for (int k = tid; k < n; k += kSelThreads) accQ[k] = __dmul_rn(srt[k], srt[k]);
+        __syncthreads();
+        if (tid == 0) running_sum(srt, accA, n);
+        else if (tid == 64) running_sum(accQ, accQ, n);
         __syncthreads();
         if (rule == kRuleBudget) {
             const double target = __dmul_rn(param, accA[n - 1]);
