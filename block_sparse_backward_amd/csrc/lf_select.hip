@@ -30,20 +30,24 @@ namespace lf {
 // t + 1), then 3 in-vector levels over e.
 // ---------------------------------------------------------------------------
 // Eight consecutive elements as floats from a raw buffer (16-byte loads; past
-// the buffer's end they read as zeros).
+// the buffer's end they read as zeros).  The loads carry the non-temporal
+// hint: each byte is read once, and streaming it through the last-level
+// cache would evict what the kernels before left there (the backward's dirty
+// outputs among it, whose write-back then competes with these reads).
+constexpr int kStreamLoad = 2;  // cache policy bits of a buffer load: nt
 template <typename T>
 __device__ __forceinline__ void load8_buf(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
                                           float (&x)[8]) {
     if constexpr (sizeof(T) == 2) {
-        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+        const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kStreamLoad);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             x[2 * j] = __uint_as_float(r[j] << 16);
             x[2 * j + 1] = __uint_as_float(r[j] & 0xffff0000u);
         }
     } else {
-        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
-        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, 0);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kStreamLoad);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, kStreamLoad);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             x[j] = __uint_as_float(a[j]);
