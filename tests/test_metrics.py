@@ -43,3 +43,16 @@ def test_flop_counts_by_brute_force(causal):
     assert metrics.bwd_flops_kept(keep, N, d, block, causal) == 10 * d * want
     assert metrics.bwd_flops_kept(np.ones_like(keep), N, d, block, causal) == \
         metrics.bwd_flops_dense(2, 3, N, d, causal)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asked for more it stops before any GPU
+    work with a message and a nonzero status."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr + r.stdout
+    assert not r.stdout.strip().startswith("{")  # no JSON line
