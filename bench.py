@@ -111,9 +111,11 @@ def main():
         """One step per seed: the forwards first, then the backward steps
         (selection, then the backward) back to back, as in a training step
         whose backward pass runs over the layers after the forward pass.  The
-        backward is the library's one call (split=False: columns fwd, select,
-        backward, 0) or its dK/dV and dQ phases as two calls, each timed
-        (split=True: columns fwd, select, dK/dV, dQ).
+        backward is the library's one call, timed with the selection as one
+        interval (split=False: columns fwd, select + backward; no event between
+        the two, since an event record on the stream delays the next launch by
+        a few microseconds), or its dK/dV and dQ phases as two calls, each
+        timed (split=True: columns fwd, select, dK/dV, dQ).
         Returns the wall time, per-step times and the selections."""
         sels = [bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev) for _ in seeds]
         evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in seeds]
@@ -130,19 +132,22 @@ def main():
             ev[0].record(stream)
             bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
                             scale=cfg.scale, heads_kv=cfg.Hkv, out=sel)
-            ev[1].record(stream)
             if split:
+                ev[1].record(stream)
                 bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DKDV, **common)
                 ev[2].record(stream)
                 bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DQ, **common)
             else:
                 bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_ALL, **common)
-                ev[2].record(stream)
             ev[3].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        ms = np.array([[f[0].elapsed_time(f[1])] + [e[i].elapsed_time(e[i + 1]) for i in range(3)]
-                       for f, e in zip(evf, evb)])
+        if split:
+            ms = np.array([[f[0].elapsed_time(f[1])] + [e[i].elapsed_time(e[i + 1]) for i in range(3)]
+                           for f, e in zip(evf, evb)])
+        else:
+            ms = np.array([[f[0].elapsed_time(f[1]), e[0].elapsed_time(e[3])]
+                           for f, e in zip(evf, evb)])
         flops = [metrics.bwd_flops_kept(s["block_w"].cpu().numpy(), cfg.N, cfg.d, cfg.block,
                                         cfg.causal) for s in sels]
         kept = [float((s["block_w"] != 0).float().mean().item()) for s in sels]
@@ -155,16 +160,18 @@ def main():
     run_steps(main_delta, list(range(10_000, 10_000 + args.warmup)))
     log(f"[bench] timing {args.steps} steps, delta={main_delta}")
     wall, ms, flops, kept = run_steps(main_delta, list(range(args.steps)))
-    # columns: fwd, select, backward (one call), 0
-    t_fwd, t_sel = ms[:, 0].mean(), ms[:, 1].mean()
-    t_bwd = float(ms[:, 2:].sum(axis=1).mean())
-    t_attn_bwd = t_sel + t_bwd
-    # the same steps with the backward's two phases timed apart (the dK/dV
-    # walk alone is the roofline kernel)
+    # columns: fwd, select + backward (one call)
+    t_fwd = ms[:, 0].mean()
+    per_step_attn = ms[:, 1]
+    t_attn_bwd = float(per_step_attn.mean())
+    # the same steps with the selection and the backward's two phases timed
+    # apart (the dK/dV walk alone is the roofline kernel)
     log(f"[bench] phase breakdown {args.steps} steps, delta={main_delta}")
     _, ms_s, flops_s, _ = run_steps(main_delta, list(range(args.steps)), split=True)
     t_kv, t_q = ms_s[:, 2].mean(), ms_s[:, 3].mean()
-    per_step_attn = ms[:, 1:].sum(axis=1)
+    t_sel = float(ms_s[:, 1].mean())
+    per_step_bwd = per_step_attn - ms_s[:, 1]  # same seeds in both passes
+    t_bwd = float(per_step_bwd.mean())
     value = F_dense / (t_attn_bwd * 1e-3) / 1e12
     log(f"[bench] fwd {t_fwd:.3f} ms, select {t_sel:.3f} ms, bwd {t_bwd:.3f} ms "
         f"(apart: dK/dV {t_kv:.3f}, dQ {t_q:.3f}), kept {kept.mean():.4f}")
@@ -184,17 +191,18 @@ def main():
     sweep_out = []
     for dl in sorted(sweep):
         ms_d, fl_d, kept_d, ms_p = sweep[dl]
-        attn_ms = float(ms_d[:, 1:].sum(axis=1).mean())
+        attn_ms = float(ms_d[:, 1].mean())
+        bwd_d = ms_d[:, 1] - ms_p[:, 1]  # the select timed in the split pass, same seeds
         sweep_out.append(dict(
-            delta=dl, steps=int(ms_d.shape[0]), select_ms=round(float(ms_d[:, 1].mean()), 4),
-            bwd_ms=round(float(ms_d[:, 2:].sum(axis=1).mean()), 4),
+            delta=dl, steps=int(ms_d.shape[0]), select_ms=round(float(ms_p[:, 1].mean()), 4),
+            bwd_ms=round(float(bwd_d.mean()), 4),
             attn_bwd_ms=round(attn_ms, 4),
-            attn_bwd_ms_min=round(float(ms_d[:, 1:].sum(axis=1).min()), 4),
-            attn_bwd_ms_max=round(float(ms_d[:, 1:].sum(axis=1).max()), 4),
+            attn_bwd_ms_min=round(float(ms_d[:, 1].min()), 4),
+            attn_bwd_ms_max=round(float(ms_d[:, 1].max()), 4),
             eff_tflops=round(F_dense / (attn_ms * 1e-3) / 1e12, 2),
             kept_fraction=round(float(kept_d.mean()), 5),
             kept_work_fraction=round(float(fl_d.mean() / F_dense), 5),
-            bwd_tflops_on_kept=round(float(fl_d.sum() / (ms_d[:, 2:].sum() * 1e-3) / 1e12), 2),
+            bwd_tflops_on_kept=round(float(fl_d.sum() / (bwd_d.sum() * 1e-3) / 1e12), 2),
             dkdv_ms=round(float(ms_p[:, 2].mean()), 4), dq_ms=round(float(ms_p[:, 3].mean()), 4),
         ))
     dense_ms = next((s["attn_bwd_ms"] for s in sweep_out if s["delta"] == 0.0), None)
@@ -223,7 +231,7 @@ def main():
                     algorithmic_flops_per_launch=float(f_kv.mean()),
                     avg_launch_ms=round(float(t_kv), 4))
     bwd_walks = dict(
-        kept_tile_mfma_frac=round(float(flops.sum() / (ms[:, 2:].sum() * 1e-3) / 1e12) / peak, 4),
+        kept_tile_mfma_frac=round(float(flops.sum() / (per_step_bwd.sum() * 1e-3) / 1e12) / peak, 4),
         note="F_kept (10 d FLOP per unmasked kept pair) / t_bwd / peak",
         dq_phase_executed_tflops=round(
             float(0.6 * flops_s.sum() / (ms_s[:, 3].sum() * 1e-3) / 1e12), 2))
@@ -305,10 +313,12 @@ def main():
         "timing": "HIP events on the launch stream, steady state (caches not flushed); the "
                   "steps' forwards run first, then their select+bwd back to back (a training "
                   "step's backward pass follows the whole forward pass); the backward is the "
-                  "library's one call (the dQ plan runs alongside the dK/dV walk); "
+                  "library's one call (the dQ plan runs alongside the dK/dV walk), timed with "
+                  "the selection as one interval (no event between them); select_ms, "
                   "bwd_phases_ms and the roofline come from a second pass over the same seeds "
-                  "with the two phases launched apart; ms_per_step is host wall time of the "
-                  "first pass per step",
+                  "with the selection and the two phases timed apart, and bwd_ms is the one "
+                  "interval less select_ms; ms_per_step is host wall time of the first pass "
+                  "per step",
     }
     print(json.dumps(out), flush=True)
 
