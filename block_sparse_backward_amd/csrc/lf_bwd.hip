@@ -194,7 +194,7 @@ constexpr int kDqMaxSlots = kDqChunkItems + 2 * kDqGrid;  // fp32 partial tiles,
 constexpr int kDqMinChunk = 16;              // key steps per chunk, at least
 constexpr int kDqChunkBelow = 2 * kDqGrid;   // chunk blocks when fewer are kept
 constexpr int kDqZeroPer = 8;                // skipped blocks per zero-fill item
-constexpr int kDqFinSplit = 2;               // finalize workgroups per chunked block
+constexpr int kDqFinSplit = 4;               // finalize workgroups per chunked block
 
 struct DqWorkspace {  // carved out of the caller's workspace
     int* ctrl;        // [0] items, [1] queue position, [2] chunked blocks
