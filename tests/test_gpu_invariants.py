@@ -1,7 +1,7 @@
 """GPU invariants of the path (through the C ABI): determinism, never-loaded
 skipped tiles (NaN poisoning), outputs fully written (NaN-filled buffers),
 nesting across budgets, degenerate heads, independence of the backward's two
-phases."""
+phases, no state shared between calls on concurrent streams."""
 import math
 
 import numpy as np
@@ -165,3 +165,46 @@ def test_delta_zero_is_the_dense_gradient():
     ref = oracle.attn_bwd_dense(q64, k64, v64, d64, cfg.scale, cfg.causal)
     for name, r in zip(("dq", "dk", "dv"), ref):
         assert max_abs_rel(host(g[name]), r) <= TOL["bf16"], name
+
+
+def test_concurrent_streams_share_no_state():
+    """Two problems of different shapes run at the same time on two streams
+    (each with its own outputs and workspace) give the bits of the same problems
+    run one after the other: the library keeps no state between calls."""
+    dev = torch.device("cuda:0")
+    cfgs = [(CFG, 0.1, 3), (CFGB64, 0.2, 4)]
+
+    def setup(cfg, delta, seed):
+        inp = make_inputs(cfg, seed)
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+        o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        sel = bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = bd.bwd_workspace(q, k, cfg.block, cfg.causal)
+        kw = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale)
+
+        def run():
+            for _ in range(3):  # repeated, so that the two streams overlap for a while
+                bd.attn_fwd(q, k, v, out=(o, lse), **kw)
+                bd.block_select(o, do, delta, seed, heads_kv=cfg.Hkv, out=sel, **kw)
+                bd.attn_bwd(q, k, v, lse, do, sel, out=grads, workspace=ws, **kw)
+
+        def outs():
+            return [_bits(t) for t in (o, lse, *grads, sel["kept_idx"], sel["block_w"])]
+        return run, outs
+
+    jobs = [setup(*c) for c in cfgs]
+    ref = []
+    for run, outs in jobs:
+        run()
+        torch.cuda.synchronize()
+        ref.append(outs())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for (run, _), s in zip(jobs, streams):
+        with torch.cuda.stream(s):
+            run()
+    torch.cuda.synchronize()
+    for (_, outs), r in zip(jobs, ref):
+        for a, b in zip(outs(), r):
+            assert np.array_equal(a, b)
