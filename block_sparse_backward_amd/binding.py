@@ -275,6 +275,34 @@ def varlen_block_offsets(cu_seqlens, block):
     return cb
 
 
+def _need_packed(items, device):
+    """Flat packed buffers of a variable-length batch, as (tensor, name,
+    numel, dtype) items: each must hold exactly `numel` elements of `dtype`,
+    contiguous, on `device`.  The library cannot see the packed lengths, so a
+    short buffer would be read or written past its end: every size is checked
+    before anything else."""
+    for t, name, numel, _ in items:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.numel() != numel:
+            raise ValueError(f"{name} holds {t.numel()} elements; cu_seqlens and the head "
+                             f"counts give {numel}")
+    for t, name, _, dtype in items:
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != device or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor on {device}, got one on {t.device}")
+
+
+def _check_cu(cu, block):
+    if len(cu) < 1 or cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0 and be nondecreasing")
+    if int(block) < 1:
+        raise ValueError("block must be >= 1")
+
+
 def _varlen_shape(cu, Hq, Hkv, d, block, causal, scale, dtype):
     return make_shape(len(cu) - 1, Hq, Hkv, 0, d, block, causal,
                       d ** -0.5 if scale is None else scale, dtype)
@@ -288,10 +316,13 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, heads_q, heads_kv, head_dim, causal=Tru
     cu, arr = _cu(cu_seqlens)
     shp = _varlen_shape(cu, heads_q, heads_kv, head_dim, block, causal, scale, q.dtype)
     dev = q.device
+    _check_cu(cu, block)
+    T = cu[-1]
+    _need_packed([(q, "q", heads_q * T * head_dim, q.dtype),
+                  (k, "k", heads_kv * T * head_dim, q.dtype),
+                  (v, "v", heads_kv * T * head_dim, q.dtype)], dev)
     o = torch.empty_like(q)
-    lse = torch.empty(heads_q * cu[-1], dtype=torch.float32, device=dev)
-    for t in (q, k, v):
-        _need(t, "tensor", t.shape, q.dtype, dev)
+    lse = torch.empty(heads_q * T, dtype=torch.float32, device=dev)
     _check(lib, lib.lf_attn_fwd_varlen(ctypes.byref(shp), arr, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                        _ptr(lse), _stream(dev)))
     return o, lse
@@ -304,10 +335,13 @@ def block_select_varlen(o, dout, cu_seqlens, heads_q, head_dim, delta, seed, blo
     tau / kept_count [Hq * B]."""
     lib = load()
     cu, arr = _cu(cu_seqlens)
+    _check_cu(cu, block)
     cb = varlen_block_offsets(cu, block)
     shp = _varlen_shape(cu, heads_q, heads_kv or heads_q, head_dim, block, causal, scale, o.dtype)
     dev = o.device
     B, nb = len(cu) - 1, cb[-1]
+    _need_packed([(o, "o", heads_q * cu[-1] * head_dim, o.dtype),
+                  (dout, "dout", heads_q * cu[-1] * head_dim, o.dtype)], dev)
     out = dict(
         D=torch.empty(heads_q * cu[-1], dtype=torch.float32, device=dev),
         mass=torch.empty(heads_q * nb, dtype=torch.float64, device=dev),
@@ -316,8 +350,6 @@ def block_select_varlen(o, dout, cu_seqlens, heads_q, head_dim, delta, seed, blo
         kept_idx=torch.empty(heads_q * nb, dtype=torch.int32, device=dev),
         kept_count=torch.empty(heads_q * B, dtype=torch.int32, device=dev),
     )
-    _need(o, "o", o.shape, o.dtype, dev)
-    _need(dout, "dout", o.shape, o.dtype, dev)
     _check(lib, lib.lf_block_select_varlen(
         ctypes.byref(shp), arr, _ptr(o), _ptr(dout), int(rule), float(delta),
         ctypes.c_uint64(int(seed) & (2**64 - 1)), _ptr(out["D"]), _ptr(out["mass"]),
@@ -334,12 +366,22 @@ def attn_bwd_varlen(q, k, v, lse, dout, sel, cu_seqlens, heads_q, heads_kv, head
     cu, arr = _cu(cu_seqlens)
     shp = _varlen_shape(cu, heads_q, heads_kv, head_dim, block, causal, scale, q.dtype)
     dev = q.device
+    _check_cu(cu, block)
+    T, B = cu[-1], len(cu) - 1
+    nb = varlen_block_offsets(cu, block)[-1]
+    _need_packed([(q, "q", heads_q * T * head_dim, q.dtype),
+                  (k, "k", heads_kv * T * head_dim, q.dtype),
+                  (v, "v", heads_kv * T * head_dim, q.dtype),
+                  (dout, "dout", heads_q * T * head_dim, q.dtype),
+                  (lse, "lse", heads_q * T, torch.float32),
+                  (sel["D"], "D", heads_q * T, torch.float32),
+                  (sel["block_w"], "block_w", heads_q * nb, torch.float32),
+                  (sel["kept_idx"], "kept_idx", heads_q * nb, torch.int32),
+                  (sel["kept_count"], "kept_count", heads_q * B, torch.int32)], dev)
     n = ctypes.c_size_t(0)
     _check(lib, lib.lf_bwd_workspace_size_varlen(ctypes.byref(shp), arr, ctypes.byref(n)))
     ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    for t in (q, k, v, dout):
-        _need(t, "tensor", t.shape, q.dtype, dev)
     _check(lib, lib.lf_attn_bwd_varlen(
         ctypes.byref(shp), arr, _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(sel["D"]),
         _ptr(sel["kept_idx"]), _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq), _ptr(dk),

@@ -35,15 +35,21 @@ COMMON = [
 ]
 
 
-def build(verbose=False, jobs=None):
-    """Compile every source (always) and link the shared library."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose=False, jobs=None, lib=LIB, objdir=OBJDIR, host_flags=()):
+    """Compile every source (always) and link the shared library `lib`.
+
+    `host_flags` are extra flags for the host half of every source only (each
+    is passed after -Xarch_host, so the gfx950 code is built as usual); the
+    sanitized build of the C-ABI layer's host code uses them."""
+    os.makedirs(objdir, exist_ok=True)
+    xhost = [f for flag in host_flags for f in ("-Xarch_host", flag)]
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *xhost, "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -58,13 +64,13 @@ def build(verbose=False, jobs=None):
             sys.stderr.write(text)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *xhost, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    shutil.move(tmp, LIB)
-    return LIB
+    shutil.move(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

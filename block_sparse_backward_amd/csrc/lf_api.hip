@@ -41,8 +41,9 @@ lf_status check_shape(const lf_shape* s, lf::Problem& pb, bool& empty) {
     if (!std::isfinite(s->scale)) return fail(LF_EINVAL, "scale must be finite");
     if (s->head_dim != 64 && s->head_dim != 128) return fail(LF_EUNSUPPORTED, "head_dim must be 64 or 128");
     if (s->block != 64 && s->block != 128) return fail(LF_EUNSUPPORTED, "block must be 64 or 128");
-    if ((s->seqlen + s->block - 1) / s->block > kMaxBlocksPerHead)
-        return fail(LF_EUNSUPPORTED, "ceil(seqlen / block) must be <= 4096");
+    // in 64 bits: seqlen + block - 1 overflows int32 for the longest lengths
+    const int64_t nqb = ((int64_t)s->seqlen + s->block - 1) / s->block;
+    if (nqb > kMaxBlocksPerHead) return fail(LF_EUNSUPPORTED, "ceil(seqlen / block) must be <= 4096");
     const double elems = (double)s->batch * s->heads_q * s->seqlen * s->head_dim;
     if (elems > 9.0e15) return fail(LF_EINVAL, "tensor too large");
     pb.B = s->batch;
@@ -51,7 +52,7 @@ lf_status check_shape(const lf_shape* s, lf::Problem& pb, bool& empty) {
     pb.N = s->seqlen;
     pb.d = s->head_dim;
     pb.block = s->block;
-    pb.nqb = (s->seqlen + s->block - 1) / s->block;  // the last block may be partial
+    pb.nqb = (int)nqb;  // the last block may be partial
     pb.causal = s->causal != 0;
     pb.scale = s->scale;
     pb.bf16 = s->dtype == LF_BF16;
@@ -113,6 +114,7 @@ const char* lf_status_str(lf_status st) {
         case LF_EINVAL: return "LF_EINVAL";
         case LF_EUNSUPPORTED: return "LF_EUNSUPPORTED";
         case LF_EHIP: return "LF_EHIP";
+        default: break;
     }
     return "unknown lf_status";
 }

@@ -1168,7 +1168,10 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
     const unsigned nwg_kv = (unsigned)(pb.B * pb.Hkv * nkt);
     const size_t nblocks = (size_t)pb.B * pb.Hq * pb.nqb;
     const float sl2 = pb.scale * kLog2e;
-    const DqWorkspace ws = dq_workspace(workspace, nblocks, pb.block, pb.d);
+    // the workspace may be NULL when only the dK/dV half runs: no pointer
+    // arithmetic on it then (the kernels get an all-NULL view they never use)
+    const DqWorkspace ws = workspace ? dq_workspace(workspace, nblocks, pb.block, pb.d)
+                                     : DqWorkspace{};
 #define LF_BWD(DD, BB, CC)                                                                      \
     if (pb.d == DD && pb.block == BB && (pb.causal != 0) == CC) {                               \
         /* with both phases, the plan rides along in the dK/dV launch where it fits */          \

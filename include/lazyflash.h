@@ -66,10 +66,15 @@ typedef enum {
     LF_OK = 0,
     LF_EINVAL = 1,        /* malformed arguments (null pointer, bad shape, delta) */
     LF_EUNSUPPORTED = 2,  /* well-formed but not implemented (head_dim, block, ...) */
-    LF_EHIP = 3           /* the HIP runtime reported an error at launch */
+    LF_EHIP = 3,          /* the HIP runtime reported an error at launch */
+    /* not a status: makes every int32_t value a valid lf_status, so a code
+     * from a newer library or a caller's cast is safe to pass around */
+    LF_STATUS_MAX_ENUM = 0x7fffffff
 } lf_status;
 
-typedef enum { LF_BF16 = 0, LF_F32 = 1 } lf_dtype;
+/* LF_DTYPE_MAX_ENUM is not a dtype: it makes every int32_t value a valid
+ * lf_dtype, so an unknown code in lf_shape is rejected, not undefined */
+typedef enum { LF_BF16 = 0, LF_F32 = 1, LF_DTYPE_MAX_ENUM = 0x7fffffff } lf_dtype;
 
 typedef struct {
     int32_t batch;      /* B */

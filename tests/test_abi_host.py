@@ -14,6 +14,15 @@ from block_sparse_backward_amd import binding as bd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lazyflash.h")
+# The library under test: the in-tree build, or (LF_ABI_TEST_LIB) a build of
+# the same sources whose host code runs under AddressSanitizer and UBSan
+# (tests/test_abi_sanitized.py).
+LIB = os.environ.get("LF_ABI_TEST_LIB", bd.LIB_PATH)
+
+
+@pytest.fixture(autouse=True)
+def _library_under_test():
+    bd.load(LIB)  # the first load fixes the library every later call uses
 
 
 def declared_functions():
@@ -23,19 +32,19 @@ def declared_functions():
 
 
 def test_library_exports_every_declared_symbol():
-    lib = bd.load()
+    lib = bd.load(LIB)
     names = declared_functions()
     assert set(names) == set(bd.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
-    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True,
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (lf_[a-z_0-9]+)$", out, flags=re.M))
     assert set(names) <= exported
 
 
 def test_abi_version_and_status_names():
-    lib = bd.load()
+    lib = bd.load(LIB)
     assert lib.lf_abi_version() == bd.ABI_VERSION
     assert lib.lf_status_str(0) == b"LF_OK"
     assert lib.lf_status_str(1) == b"LF_EINVAL"
@@ -90,9 +99,10 @@ def _ws_size(lib, shp):
     (dict(block=32), bd.LF_EUNSUPPORTED),
     (dict(seqlen=128 * 4096 + 1), bd.LF_EUNSUPPORTED),   # 4097 blocks, the last partial
     (dict(seqlen=128 * 4097), bd.LF_EUNSUPPORTED),
+    (dict(seqlen=2**31 - 1), bd.LF_EUNSUPPORTED),        # block count in 64 bits
 ])
 def test_bad_shapes_rejected_by_every_entry_point(kw, status):
-    lib = bd.load()
+    lib = bd.load(LIB)
     shp = _shape(**kw)
     assert _fwd(lib, shp) == status
     assert lib.lf_last_error() != b""
@@ -102,7 +112,7 @@ def test_bad_shapes_rejected_by_every_entry_point(kw, status):
 
 
 def test_null_shape_and_null_pointers():
-    lib = bd.load()
+    lib = bd.load(LIB)
     assert lib.lf_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == bd.LF_EINVAL
     assert _fwd(lib, _shape(), ptr=NULL) == bd.LF_EINVAL
     assert b"NULL" in lib.lf_last_error()
@@ -112,13 +122,13 @@ def test_null_shape_and_null_pointers():
 
 @pytest.mark.parametrize("delta", [-0.01, 1.0, 2.0, math.nan, math.inf])
 def test_select_rejects_bad_delta(delta):
-    lib = bd.load()
+    lib = bd.load(LIB)
     assert _sel(lib, _shape(), delta) == bd.LF_EINVAL
     assert b"delta" in lib.lf_last_error()
 
 
 def test_empty_problems_are_noops():
-    lib = bd.load()
+    lib = bd.load(LIB)
     for kw in (dict(batch=0), dict(seqlen=0)):
         shp = _shape(**kw)
         assert _fwd(lib, shp, ptr=NULL) == bd.LF_OK
@@ -135,7 +145,7 @@ def test_binding_rejects_unsupported_dtype():
 
 
 def test_bwd_phase_mask_checked():
-    lib = bd.load()
+    lib = bd.load(LIB)
     shp = _shape()
 
     def call(mask, dq=FAKE, dk=FAKE, dv=FAKE):
@@ -151,7 +161,7 @@ def test_bwd_phase_mask_checked():
 
 
 def test_workspace_size_and_checks():
-    lib = bd.load()
+    lib = bd.load(LIB)
     # bf16: fp32 partial tiles of 1536 blocks plus the item and block tables
     shp = _shape(batch=2, heads_q=4, heads_kv=2, seqlen=1024, head_dim=128, block=128)
     st, n = _ws_size(lib, shp)
@@ -197,7 +207,7 @@ def test_wrapper_and_binding_reject_host_tensors():
 def test_ragged_seqlen_passes_validation():
     # N not a multiple of the block: the last query block is partial; the shape
     # is valid, so only the NULL tensor pointers are reported
-    lib = bd.load()
+    lib = bd.load(LIB)
     shp = _shape(seqlen=200)
     assert _fwd(lib, shp, ptr=NULL) == bd.LF_EINVAL
     assert b"NULL" in lib.lf_last_error()
@@ -221,16 +231,20 @@ def _varlen(lib, shp, cu, ptr=FAKE):
     ([1, 5, 9], bd.LF_EINVAL),                 # must start at 0
     ([0, 300, 200], bd.LF_EINVAL),             # decreasing
     ([0, 300, 300 + 128 * 4096 + 1], bd.LF_EUNSUPPORTED),  # one sequence too long
+    ([0, 100, 50, 200], bd.LF_EINVAL),         # decreasing in the middle
+    ([0, -5], bd.LF_EINVAL),                   # a negative length
+    ([0, 2**31 - 1], bd.LF_EUNSUPPORTED),      # the longest int32 length
+    ([0, 64, 2**31 - 1, 2**31 - 1], bd.LF_EUNSUPPORTED),
 ])
 def test_varlen_bad_offsets_rejected_before_any_launch(cu, status):
-    lib = bd.load()
+    lib = bd.load(LIB)
     shp = _shape(batch=len(cu) - 1, seqlen=0)
     f, s, b, w, _ = _varlen(lib, shp, cu)
     assert f == s == b == w == status
 
 
 def test_varlen_null_offsets_and_pointers():
-    lib = bd.load()
+    lib = bd.load(LIB)
     shp = _shape(batch=2, seqlen=0)
     assert _varlen(lib, shp, None)[:4] == (bd.LF_EINVAL,) * 4
     f, s, b, w, n = _varlen(lib, shp, [0, 100, 356], ptr=NULL)
@@ -242,9 +256,49 @@ def test_varlen_null_offsets_and_pointers():
 
 
 def test_varlen_bad_rule_parameter():
-    lib = bd.load()
+    lib = bd.load(LIB)
     shp = _shape(batch=1, seqlen=0)
     arr = (ctypes.c_int32 * 2)(0, 256)
     for rule, param in ((0, 1.0), (1, 0.0), (2, 1.5), (9, 0.5)):
         assert lib.lf_block_select_varlen(ctypes.byref(shp), arr, FAKE, FAKE, rule, param, 0,
                                           FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == bd.LF_EINVAL
+
+
+def test_varlen_binding_checks_packed_sizes_before_any_call():
+    # The C ABI cannot see how long the packed buffers are, so the binding
+    # checks every buffer against cu_seqlens first: a cu_seqlens whose total
+    # exceeds the tensors is a ValueError (host tensors here: the size check
+    # comes before the device check, and nothing reaches the library).
+    Hq, Hkv, d, blk = 4, 2, 64, 64
+    cu = [0, 100, 356]
+    T = cu[-1]
+    nb = sum(-(-(b - a) // blk) for a, b in zip(cu, cu[1:]))
+    q = torch.zeros(Hq * T * d, dtype=torch.bfloat16)
+    kv = torch.zeros(Hkv * T * d, dtype=torch.bfloat16)
+    long_cu = [0, 100, 357]
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.attn_fwd_varlen(q, kv, kv, long_cu, Hq, Hkv, d, block=blk)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.block_select_varlen(q, q, long_cu, Hq, d, 0.1, 0, block=blk, heads_kv=Hkv)
+    sel = dict(D=torch.zeros(Hq * T), block_w=torch.zeros(Hq * nb),
+               kept_idx=torch.zeros(Hq * nb, dtype=torch.int32),
+               kept_count=torch.zeros(Hq * 2, dtype=torch.int32))
+    lse = torch.zeros(Hq * T)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        bd.attn_bwd_varlen(q, kv, kv, lse, q, sel, long_cu, Hq, Hkv, d, block=blk)
+    # every per-head and per-block array is checked too
+    for key, n in (("D", Hq * T - 1), ("block_w", Hq * nb + 1), ("kept_idx", 3),
+                   ("kept_count", Hq * 3)):
+        bad = dict(sel)
+        bad[key] = torch.zeros(n, dtype=sel[key].dtype)
+        with pytest.raises(ValueError, match=key):
+            bd.attn_bwd_varlen(q, kv, kv, lse, q, bad, cu, Hq, Hkv, d, block=blk)
+    with pytest.raises(ValueError, match="lse"):
+        bd.attn_bwd_varlen(q, kv, kv, lse[:-1], q, sel, cu, Hq, Hkv, d, block=blk)
+    with pytest.raises(ValueError, match="k holds"):
+        bd.attn_bwd_varlen(q, q, kv, lse, q, sel, cu, Hq, Hkv, d, block=blk)
+    with pytest.raises(ValueError, match="nondecreasing"):
+        bd.attn_fwd_varlen(q, kv, kv, [0, 300, 200], Hq, Hkv, d, block=blk)
+    # right sizes: only then does the device check refuse the host tensors
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bd.attn_bwd_varlen(q, kv, kv, lse, q, sel, cu, Hq, Hkv, d, block=blk)

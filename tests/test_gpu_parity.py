@@ -53,9 +53,13 @@ SMALL = {
 def test_small_full_parity(name):
     cfg, delta = SMALL[name]
     print(f"[parity] {name} {cfg} delta={delta}", flush=True)
-    inp = make_inputs(cfg, 0)
-    gpu = run_gpu(cfg, inp, delta, seed=0)
-    ref_sel = check_select_exact(cfg, inp, gpu, delta, 0)
+    _check_full(cfg, make_inputs(cfg, 0), delta, seed=0, tag=name)
+
+
+def _check_full(cfg, inp, delta, seed, tag):
+    """Every element of O, LSE, D (kept rows), dQ, dK, dV against the oracle."""
+    gpu = run_gpu(cfg, inp, delta, seed=seed)
+    ref_sel = check_select_exact(cfg, inp, gpu, delta, seed)
     q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
     o_ref, lse_ref = oracle.attn_fwd(q64, k64, v64, cfg.scale, cfg.causal)
     tol = TOL[cfg.dtype]
@@ -70,13 +74,37 @@ def test_small_full_parity(name):
         assert max_abs_rel(d_gpu[kept_rows], d_ref[kept_rows]) <= tol
     assert np.all(d_gpu[~kept_rows] == 0.0)
     dq, dk, dv = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, ref_sel["keep"],
-                                        ref_sel["w"], cfg.scale, cfg.causal)
+                                        ref_sel["w"], cfg.scale, cfg.causal, o=o_ref, lse=lse_ref)
     errs = [max_abs_rel(host(gpu[n]), r) for n, r in (("dq", dq), ("dk", dk), ("dv", dv))]
-    print(f"[parity] {name} kept={ref_sel['keep'].mean():.3f} errs={errs}", flush=True)
+    print(f"[parity] {tag} kept={ref_sel['keep'].mean():.3f} errs={errs}", flush=True)
     assert max(errs) <= tol, errs
     # rows of skipped blocks of dq are exact zeros
     skipped = np.repeat(~ref_sel["keep"], cfg.block, axis=2)[:, :, :cfg.N]
     assert np.all(host(gpu["dq"])[skipped] == 0.0)
+    return ref_sel
+
+
+# Causal heads that keep more than 64 blocks: the dK/dV walk holds a head's
+# kept list 64 entries at a time in a register, so these walks reload it in
+# mid-walk (key tile 0 walks 96 or 128 blocks per head) and the later key
+# tiles find their first block past the first 64 entries.  Every element is
+# compared, for 128- and 64-row blocks and both head dims.
+LONG_WALKS = {
+    "causal_96_blocks_per_head_d128_b128": Config("w1", 1, 2, 1, 96 * 128, 128, "bf16", True,
+                                                   128, 1.5),
+    "causal_128_blocks_per_head_d128_b64": Config("w2", 1, 2, 1, 128 * 64, 128, "bf16", True,
+                                                   64, 1.5),
+    "causal_130_blocks_per_head_d64_b64_ragged": Config("w3", 1, 4, 2, 130 * 64 - 20, 64, "bf16",
+                                                         True, 64, 1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_WALKS))
+def test_long_causal_walk_parity(name):
+    cfg = LONG_WALKS[name]
+    print(f"[parity-walk] {name} {cfg} delta=0", flush=True)
+    ref_sel = _check_full(cfg, make_inputs(cfg, 0), 0.0, seed=0, tag=name)
+    assert ref_sel["kept_count"].min() > 64
 
 
 # Softmax scales other than 1/sqrt(d): a negative scale (the forward negates Q
@@ -122,13 +150,21 @@ def _full_inputs(name):
 
 
 FULL = [(n, dl) for n in ("mid", "headline", "long", "noncausal") for dl in CONFIGS[n].deltas]
+# Whole-group comparisons (every key of dK/dV, every kept block of dQ) where
+# the oracle finishes in tens of seconds: one GQA group of mid at every delta
+# and of the headline at delta 0.1 and 0.2 (about 45 and 30 kept blocks of
+# 32768-key rows).  The headline at delta 0 (1024 kept blocks in the group)
+# and the long shape (about 800) compare the tail keys that only the sampled
+# blocks reach, plus the size-free invariants; their walks take the same code
+# paths as the whole-group and long-walk cases.
+WHOLE_GROUP = {("mid", 0.0), ("mid", 0.05), ("mid", 0.1), ("headline", 0.1), ("headline", 0.2)}
 
 
 @pytest.mark.parametrize("name,delta", FULL)
 def test_full_size_parity(name, delta):
     cfg, inp = _full_inputs(name)
     print(f"[parity-full] {name} delta={delta}", flush=True)
-    _check_large(cfg, inp, delta)
+    _check_large(cfg, inp, delta, whole_group=(name, delta) in WHOLE_GROUP)
 
 
 # The largest supported block count per head (4096) with 64-row blocks:
@@ -157,7 +193,7 @@ def test_max_block_count_parity(name):
     _check_large(cfg, inp, 0.1)
 
 
-def _check_large(cfg, inp, delta):
+def _check_large(cfg, inp, delta, whole_group=False):
     name = cfg.name
     gpu = run_gpu(cfg, inp, delta, seed=0)
     ref_sel = check_select_exact(cfg, inp, gpu, delta, 0)
@@ -180,7 +216,7 @@ def _check_large(cfg, inp, delta):
     q64, k64, v64, d64 = (to_f64(inp[n]) for n in ("q", "k", "v", "dout"))
     keep = ref_sel["keep"]
     nqb = cfg.nqb
-    if cfg.causal:
+    if cfg.causal and not whole_group:
         # dQ of sampled kept blocks (each block's dq depends on that block
         # only), and dK/dV of the keys at and after block jt: under the causal
         # mask only query blocks >= jt reach them, and all of those that are
@@ -210,10 +246,15 @@ def _check_large(cfg, inp, delta):
         e_dk = max_abs_rel(host(gpu["dk"][b, g, tail]), dk[b, g, tail])
         e_dv = max_abs_rel(host(gpu["dv"][b, g, tail]), dv[b, g, tail])
     else:
+        # the whole group: dK/dV of every key, dQ of every row of its heads
+        # (the rows of skipped blocks are exact zeros on both sides)
         dq, dk, dv = oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, keep, ref_sel["w"],
                                             cfg.scale, cfg.causal, heads=heads)
         hs = [h for _, h in heads]
-        e_dq = max_abs_rel(host(gpu["dq"][b, hs]), dq[b, hs])
+        dq_gpu = host(gpu["dq"][b, hs])
+        e_dq = max_abs_rel(dq_gpu, dq[b, hs])
+        skipped = np.repeat(~keep[b, hs], cfg.block, axis=1)[:, :cfg.N]
+        assert np.all(dq_gpu[skipped] == 0.0)
         e_dk = max_abs_rel(host(gpu["dk"][b, g]), dk[b, g])
         e_dv = max_abs_rel(host(gpu["dv"][b, g]), dv[b, g])
     print(f"[parity-full] {name} delta={delta} kept={kept_frac:.4f} fwd={err_o:.2e} "
