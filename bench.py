@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--ceiling-reps", type=int, default=5,
                     help="timed reps of the vendor bf16 GEMM that measures the practical MFMA "
                          "ceiling of this GPU (0: skip)")
+    ap.add_argument("--config-steps", type=int, default=3,
+                    help="timed steps per delta of each other configuration in the line's "
+                         "'configs' array (0: skip them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds spent on the oracle baseline sample")
@@ -269,6 +272,15 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inp, main_delta, args.cpu_budget_s, metrics)
 
+    # the other workloads, each at its deltas: compact rows (the headline's own
+    # deltas are in delta_sweep above)
+    others_cfg = None
+    if args.config_steps > 0:
+        del q, k, v, do, o, lse, dq, dk, dv, ws, inp
+        torch.cuda.empty_cache()
+        others_cfg = [row for name in ("tiny", "mid", "long", "noncausal") if name != cfg.name
+                      for row in config_rows(CONFIGS[name], args.config_steps, peak)]
+
     out = {
         "metric": f"attention-bwd effective dense-equivalent TFLOP/s (select + sparse bwd, one "
                   f"layer) at N={cfg.N}, delta={main_delta}",
@@ -310,6 +322,7 @@ def main():
         "other_kernels": others,
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
+        "configs": others_cfg,
         "timing": "HIP events on the launch stream, steady state (caches not flushed); the "
                   "steps' forwards run first, then their select+bwd back to back (a training "
                   "step's backward pass follows the whole forward pass); the backward is the "
@@ -321,6 +334,79 @@ def main():
                   "per step",
     }
     print(json.dumps(out), flush=True)
+
+
+def config_rows(cfg, steps, peak):
+    """One compact row per delta of workload `cfg`: select + backward (the
+    library's one call) per microbatch, effective dense-equivalent TFLOP/s,
+    the kept fractions, and the dK/dV walk alone (timed in a second pass over
+    the same seeds) with its roofline fraction on its algorithmic work
+    (0.8 F_kept; bf16 only, the fp32 path does not use the matrix cores)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_backward_amd import binding as bd
+    from block_sparse_backward_amd import metrics
+    from block_sparse_backward_amd.synth import make_inputs
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] config {cfg.name}: generating")
+    inp = make_inputs(cfg, 0)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    del inp
+    o, lse = bd.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, block=cfg.block)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = bd.bwd_workspace(q, k, cfg.block, cfg.causal)
+    stream = torch.cuda.current_stream(dev)
+    common = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv),
+                  workspace=ws)
+    F_dense = metrics.bwd_flops_dense(cfg.B, cfg.Hq, cfg.N, cfg.d, cfg.causal)
+
+    def select(delta, seed, sel):
+        return bd.block_select(o, do, delta, seed, block=cfg.block, causal=cfg.causal,
+                               scale=cfg.scale, heads_kv=cfg.Hkv, out=sel)
+
+    rows = []
+    for delta in cfg.deltas:
+        log(f"[bench] config {cfg.name} delta={delta}")
+        seeds = list(range(steps))
+        sels = [bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev) for _ in seeds]
+        select(delta, 30_000, sels[0])
+        bd.attn_bwd(q, k, v, lse, do, sels[0], **common)  # warm-up
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in seeds]
+        torch.cuda.synchronize()
+        for seed, sel, e in zip(seeds, sels, ev):  # select + backward, one call
+            e[0].record(stream)
+            select(delta, seed, sel)
+            bd.attn_bwd(q, k, v, lse, do, sel, **common)
+            e[1].record(stream)
+        for seed, sel, e in zip(seeds, sels, ev):  # the same seeds, phases apart
+            select(delta, seed, sel)
+            e[2].record(stream)
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DKDV, **common)
+            e[3].record(stream)
+            bd.attn_bwd(q, k, v, lse, do, sel, phases=bd.BWD_DQ, **common)
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[3].elapsed_time(e[4])]
+                      for e in ev])
+        flops = np.array([metrics.bwd_flops_kept(s["block_w"].cpu().numpy(), cfg.N, cfg.d,
+                                                 cfg.block, cfg.causal) for s in sels], dtype=float)
+        kept = float(np.mean([(s["block_w"] != 0).float().mean().item() for s in sels]))
+        row = dict(workload=cfg.name, B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, N=cfg.N, d=cfg.d,
+                   block=cfg.block, causal=cfg.causal, dtype=cfg.dtype, delta=delta,
+                   steps=steps, attn_bwd_ms=round(float(t[:, 0].mean()), 4),
+                   eff_tflops=round(F_dense / (t[:, 0].mean() * 1e-3) / 1e12, 2),
+                   kept_fraction=round(kept, 5),
+                   kept_work_fraction=round(float(flops.mean() / F_dense), 5),
+                   dkdv_ms=round(float(t[:, 1].mean()), 4), dq_ms=round(float(t[:, 2].mean()), 4))
+        if cfg.dtype == "bf16":
+            dkdv_tf = float(0.8 * flops.sum() / (t[:, 1].sum() * 1e-3) / 1e12)
+            row["dkdv_roofline_frac"] = round(dkdv_tf / peak, 4)
+        rows.append(row)
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return rows
 
 
 def mfma_ceiling(reps, peak, n=16384):
@@ -455,19 +541,51 @@ def training_step_report(cfg, q, k, v, do, delta, steps):
                     "step speedup at amdahl_bound"}
 
 
-def cpu_baseline(cfg, inp, delta, budget_s, metrics):
-    """The oracle, timed on the host cores on whole GQA groups of the same
-    workload until about `budget_s` seconds are spent."""
-    import numpy as np
+def host_description():
+    """Cores this process may run on, the CPU model and the BLAS library
+    NumPy calls (with its thread count)."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
     try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        import numpy  # noqa: F401  (loads the BLAS that threadpoolctl reports)
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = "%s %s, %s kernels (%s)" % (
+                    p.get("internal_api"), p.get("version"), p.get("architecture"),
+                    os.path.basename(p.get("filepath", "")))
+                threads = p.get("num_threads")
+                break
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+    return cores, model, blas, threads
+
+
+def cpu_baseline(cfg, inp, delta, budget_s, metrics):
+    """The oracle, timed on the host cores, in two legs on the same workload:
+    selection + sparse backward on whole GQA groups until about `budget_s`
+    seconds are spent (the reported value), and the dense backward -- the
+    oracle's backward with every block kept at weight 1, i.e. delta = 0 --
+    on query blocks of one head until about budget_s / 2 seconds are spent.
+    Both are given as dense-equivalent TFLOP/s (the metric's unit) and as the
+    time one microbatch would take at that rate."""
+    import numpy as np
+
     import oracle
     from block_sparse_backward_amd.synth import to_f64
 
+    cores, model, blas, blas_threads = host_description()
     G = cfg.Hq // cfg.Hkv
+    F_layer = metrics.bwd_flops_dense(cfg.B, cfg.Hq, cfg.N, cfg.d, cfg.causal)
     spent = 0.0
     heads_done = 0
     groups = [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
@@ -488,12 +606,48 @@ def cpu_baseline(cfg, inp, delta, budget_s, metrics):
         if spent >= budget_s:
             break
     f_sample = metrics.bwd_flops_dense(1, heads_done, cfg.N, cfg.d, cfg.causal)
-    return {"value": round(f_sample / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    rate = f_sample / spent
+
+    # dense leg: query blocks of head (0, 0) in a seeded random order (the
+    # oracle's cost per block does not depend on its position, its causal
+    # work does: a spread sample gives the head's average), every one kept
+    # with weight 1
+    log(f"[bench] cpu baseline: dense oracle backward, ~{budget_s / 2:.0f}s budget")
+    q64 = to_f64(inp["q"][0:1, 0:1])
+    d64 = to_f64(inp["dout"][0:1, 0:1])
+    k64 = to_f64(inp["k"][0:1, 0:1])
+    v64 = to_f64(inp["v"][0:1, 0:1])
+    nqb = cfg.nqb
+    keep = np.zeros((1, 1, nqb), dtype=bool)
+    w1 = np.ones((1, 1, nqb), dtype=np.float32)
+    d_spent, d_flops, nblk = 0.0, 0, 0
+    for i in np.random.Generator(np.random.PCG64(0)).permutation(nqb):
+        keep[:] = False
+        keep[0, 0, i] = True
+        t0 = time.perf_counter()
+        oracle.attn_bwd_sparse(q64, k64, v64, d64, cfg.block, keep, w1, cfg.scale, cfg.causal)
+        d_spent += time.perf_counter() - t0
+        d_flops += metrics.bwd_flops_kept(keep, cfg.N, cfg.d, cfg.block, cfg.causal)
+        nblk += 1
+        if d_spent >= budget_s / 2:
+            break
+    d_rate = d_flops / d_spent
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{heads_done} of {cfg.B * cfg.Hq} query heads ({heads_done // G} GQA "
                       f"groups), select + sparse backward at delta={delta}, seed 0, fp64 NumPy; "
                       f"{spent:.1f} s; value = dense-equivalent FLOPs of the sampled heads / time",
-            "seconds": round(spent, 2)}
+            "seconds": round(spent, 2),
+            "ms_per_microbatch": round(F_layer / rate * 1e3, 1),
+            "dense_bwd": {"value": round(d_rate / 1e12, 6), "unit": "TFLOP/s",
+                          "sample": f"{nblk} of {nqb} query blocks of one head (seeded "
+                                    f"random order), every block kept with weight 1 "
+                                    f"(the oracle's delta = 0 backward); {d_spent:.1f} s",
+                          "seconds": round(d_spent, 2),
+                          "ms_per_microbatch": round(F_layer / d_rate * 1e3, 1)},
+            "cpu_model": model, "blas": blas, "blas_threads": blas_threads,
+            "cores_note": "cores = len(os.sched_getaffinity(0)); NumPy's BLAS runs "
+                          "blas_threads threads, the rest of the oracle one"}
 
 
 if __name__ == "__main__":
