@@ -14,16 +14,17 @@ import torch
 __all__ = ["LazyFlashError", "LfShape", "load", "make_shape", "attn_fwd", "block_select",
            "select_outputs", "attn_bwd", "bwd_workspace_bytes", "bwd_workspace",
            "EXPORTED_SYMBOLS", "LIB_PATH", "attn_fwd_varlen", "block_select_varlen",
-           "attn_bwd_varlen", "varlen_block_offsets"]
+           "attn_bwd_varlen", "varlen_block_offsets", "attn_bwd_noalloc"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyflash.so")
-ABI_VERSION = 6
+ABI_VERSION = 7
 LF_OK, LF_EINVAL, LF_EUNSUPPORTED, LF_EHIP = 0, 1, 2, 3
 LF_BF16, LF_F32 = 0, 1
 EXPORTED_SYMBOLS = ("lf_attn_fwd", "lf_block_select", "lf_block_select_rule", "lf_attn_bwd",
                     "lf_bwd_workspace_size", "lf_attn_fwd_varlen", "lf_block_select_varlen",
                     "lf_bwd_workspace_size_varlen", "lf_attn_bwd_varlen",
-                    "lf_attn_bwd_phases", "lf_status_str", "lf_last_error", "lf_abi_version")
+                    "lf_attn_bwd_phases", "lf_attn_bwd_noalloc", "lf_status_str",
+                    "lf_last_error", "lf_abi_version")
 BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 3
 SELECT_BUDGET, SELECT_FRACTION, SELECT_TOPK = 0, 1, 2
 
@@ -69,6 +70,8 @@ def load(path=LIB_PATH):
     lib.lf_attn_bwd_phases.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, Z,
                                        ctypes.c_uint32, P]
     lib.lf_attn_bwd_phases.restype = I32
+    lib.lf_attn_bwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.lf_attn_bwd_noalloc.restype = I32
     CU = ctypes.POINTER(ctypes.c_int32)
     lib.lf_attn_fwd_varlen.argtypes = [S, CU, P, P, P, P, P, P]
     lib.lf_attn_fwd_varlen.restype = I32
@@ -254,6 +257,37 @@ def attn_bwd(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=No
         _check(lib, lib.lf_attn_bwd(*args, _stream(dev)))
     else:
         _check(lib, lib.lf_attn_bwd_phases(*args, ctypes.c_uint32(phases), _stream(dev)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, lse, dout, sel, block=128, causal=True, scale=None, out=None):
+    """attn_bwd without a workspace: the library's static device scratch of
+    this GPU serves the dQ phase (lf_attn_bwd_noalloc; calls that overlap on
+    one GPU race).  Returns (dq, dk, dv); `out` optionally gives them
+    preallocated, and then nothing is allocated at all."""
+    lib = load()
+    shp, _ = _shape_from(q, k, block, causal, scale)
+    dev = q.device
+    B, Hq, N, d = q.shape
+    nqb = -(-N // block)
+    _need(k, "k", (B, shp.heads_kv, N, d), q.dtype, dev)
+    _need(v, "v", k.shape, q.dtype, dev)
+    _need(dout, "dout", q.shape, q.dtype, dev)
+    _need(lse, "lse", (B, Hq, N), torch.float32, dev)
+    _need(sel["D"], "D", (B, Hq, N), torch.float32, dev)
+    _need(sel["kept_idx"], "kept_idx", (B, Hq, nqb), torch.int32, dev)
+    _need(sel["kept_count"], "kept_count", (B, Hq), torch.int32, dev)
+    _need(sel["block_w"], "block_w", (B, Hq, nqb), torch.float32, dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _need(dq, "dq", q.shape, q.dtype, dev)
+    _need(dk, "dk", k.shape, q.dtype, dev)
+    _need(dv, "dv", k.shape, q.dtype, dev)
+    _check(lib, lib.lf_attn_bwd_noalloc(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(lse),
+                                        _ptr(dout), _ptr(sel["D"]), _ptr(sel["kept_idx"]),
+                                        _ptr(sel["kept_count"]), _ptr(sel["block_w"]), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _stream(dev)))
     return dq, dk, dv
 
 

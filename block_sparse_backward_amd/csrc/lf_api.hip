@@ -205,6 +205,28 @@ lf_status lf_attn_bwd(const lf_shape* s, const void* q, const void* k, const voi
                               workspace, workspace_bytes, LF_BWD_ALL, stream);
 }
 
+lf_status lf_attn_bwd_noalloc(const lf_shape* s, const void* q, const void* k, const void* v,
+                              const float* lse, const void* dout, const float* D,
+                              const int32_t* kept_idx, const int32_t* kept_count,
+                              const float* block_w, void* dq, void* dk, void* dv, void* stream) {
+    lf::Problem pb;
+    bool empty;
+    lf_status st = check_shape(s, pb, empty);
+    if (st != LF_OK) return st;
+    if (empty) return hip_status(hipSuccess);
+    if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv}))
+        return fail(LF_EINVAL, "NULL tensor pointer");
+    const size_t need = lf::bwd_workspace_bytes(pb), have = lf::static_scratch_bytes();
+    if (need > have) {
+        std::snprintf(g_err, sizeof(g_err),
+                      "the problem needs %zu bytes of scratch, more than the %zu bytes of the "
+                      "static scratch (use lf_attn_bwd with a workspace)", need, have);
+        return LF_EUNSUPPORTED;
+    }
+    return hip_status(lf::launch_bwd_static(pb, q, k, v, lse, dout, D, kept_idx, kept_count,
+                                            block_w, dq, dk, dv, (hipStream_t)stream));
+}
+
 // ---------------------------------------------------------------------------
 // Variable-length batches (layouts in lazyflash.h): one launch sequence per
 // sequence on the caller's stream, each sequence a fixed-length problem of

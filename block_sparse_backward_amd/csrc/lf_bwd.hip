@@ -45,6 +45,8 @@
 //   of dQ += dS K; K^T comes from transposing LDS reads.  A one-chunk block
 //   writes its dq rows; chunks write fp32 partials that the finalize pass adds
 //   in chunk order.  The queue position is the only atomic.
+#include <mutex>
+
 #include "lf_common.h"
 #include "lf_internal.h"
 #include "lf_tile.h"
@@ -1131,6 +1133,60 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Static scratch, for callers that cannot allocate: the dQ phase's workspace
+// in a file-scope device array of fixed size.  Every GPU the library runs on
+// holds its own copy at its own address until the process ends.  On the host
+// the array's name is only a stand-in for the symbol: its device address is
+// looked up once per device, with that device current, and only that address
+// is ever passed to kernels.  The workspace needs no clearing (the dQ plan
+// writes every word the walk and the finalize read), and every call on one
+// GPU shares its array, so calls that overlap on one GPU race.
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up on first use.
+hipError_t static_scratch(int device, void** ptr) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
+}
+}  // namespace
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t launch_bwd_static(const Problem& pb, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dout, const float* D,
+                             const int32_t* kept_idx, const int32_t* kept_count,
+                             const float* block_w, void* dq, void* dk, void* dv, hipStream_t st) {
+    int device = 0;
+    hipError_t e = hipStreamGetDevice(st, &device);  // the stream's GPU (NULL: the current one)
+    if (e != hipSuccess) return e;
+    void* ws = nullptr;
+    if ((e = static_scratch(device, &ws)) != hipSuccess) return e;
+    return launch_bwd(pb, q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv, ws,
+                      1u | 2u, st);
+}
+
 size_t bwd_workspace_bytes(const Problem& pb) {
     if (!pb.bf16) return 0;
     return dq_workspace_bytes((size_t)pb.B * pb.Hq * pb.nqb, pb.block, pb.d);

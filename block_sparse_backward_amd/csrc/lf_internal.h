@@ -34,6 +34,15 @@ hipError_t launch_bwd(const Problem& pb, const void* q, const void* k, const voi
 // Device workspace bytes of launch_bwd for a validated problem (0 for fp32).
 size_t bwd_workspace_bytes(const Problem& pb);
 
+// launch_bwd (both phases) with the workspace in the library's static device
+// scratch of the stream's GPU (no allocation); the problem's workspace must fit
+// static_scratch_bytes().
+size_t static_scratch_bytes();
+hipError_t launch_bwd_static(const Problem& pb, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dout, const float* D,
+                             const int32_t* kept_idx, const int32_t* kept_count,
+                             const float* block_w, void* dq, void* dk, void* dv, hipStream_t st);
+
 // Workgroup -> work-item maps that keep every workgroup of one key/value head
 // group on one XCD (workgroups are dispatched round-robin over the 8 XCDs, each
 // with its own L2), so the K/V, Q and dO tiles a group shares stay in one L2.

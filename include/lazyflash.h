@@ -36,9 +36,11 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; outputs are
  *     fully overwritten (never accumulated into).  The library allocates
  *     nothing and keeps no state between calls; scratch memory, where an entry
- *     point needs it, is a caller-owned workspace argument.  Work is enqueued
- *     on `stream` (a hipStream_t; NULL = the default stream) and the call
- *     returns without waiting for it.
+ *     point needs it, is a caller-owned workspace argument.  The one exception
+ *     is lf_attn_bwd_noalloc, for callers that cannot allocate: its scratch is
+ *     a static device array of the library (one per GPU, loaded with the
+ *     library's kernels).  Work is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream) and the call returns without waiting for it.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failed check returns LF_EINVAL (malformed) or LF_EUNSUPPORTED (valid
  *     but outside what the kernels implement) and launches nothing.  A failed
@@ -212,6 +214,26 @@ lf_status lf_attn_bwd_phases(const lf_shape* shape, const void* q, const void* k
                              size_t workspace_bytes, uint32_t phases, void* stream);
 
 /*
+ * lf_attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same backward, with the dQ phase's workspace taken from a static device
+ * array of the library (128 MiB per GPU, held until the process ends; the
+ * headline shape B=1, Hq=32, N=32768, d=128, block=128 needs 96.3 MiB) instead
+ * of a workspace argument.  Arguments, results and determinism are those of
+ * lf_attn_bwd; nothing is allocated and nothing needs clearing.  The first call
+ * on a GPU looks up that GPU's array address once (make it before capturing a
+ * graph).  Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (other streams, other threads) race; serialise them or use
+ * lf_attn_bwd with workspaces of their own.  A problem whose workspace
+ * (lf_bwd_workspace_size) exceeds the array is LF_EUNSUPPORTED, before
+ * anything is enqueued.
+ */
+lf_status lf_attn_bwd_noalloc(const lf_shape* shape, const void* q, const void* k, const void* v,
+                              const float* lse, const void* dout, const float* D,
+                              const int32_t* kept_idx, const int32_t* kept_count,
+                              const float* block_w, void* dq, void* dk, void* dv, void* stream);
+
+/*
  * Variable-length batches (a batch of sequences of different lengths, packed
  * without padding: the pages' workload is examples cut to each length, section
  * "À 32 000 tokens, 5,72 fois sur l'attention arrière" of the LazyFlash entry).
@@ -259,7 +281,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 6  /* 6: D is written on the rows of kept blocks only */
+#define LF_ABI_VERSION 7  /* 7: lf_attn_bwd_noalloc; 6: D on kept rows only */
 
 #ifdef __cplusplus
 }

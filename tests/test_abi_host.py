@@ -302,3 +302,25 @@ def test_varlen_binding_checks_packed_sizes_before_any_call():
     # right sizes: only then does the device check refuse the host tensors
     with pytest.raises(ValueError, match="GPU tensor"):
         bd.attn_bwd_varlen(q, kv, kv, lse, q, sel, cu, Hq, Hkv, d, block=blk)
+
+
+def test_noalloc_backward_checks_before_any_launch():
+    lib = bd.load(LIB)
+
+    def call(shp, ptr=FAKE):
+        return lib.lf_attn_bwd_noalloc(ctypes.byref(shp), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                       ptr, ptr, ptr, ptr, NULL)
+    assert call(_shape(heads_q=3)) == bd.LF_EINVAL
+    assert call(_shape(head_dim=96)) == bd.LF_EUNSUPPORTED
+    assert call(_shape(), ptr=NULL) == bd.LF_EINVAL
+    assert call(_shape(batch=0), ptr=NULL) == bd.LF_OK
+    # a problem whose workspace exceeds the static scratch (128 MiB): 2**27
+    # blocks need 30 bytes each in the dQ tables alone
+    big = _shape(batch=512, heads_q=64, heads_kv=8, seqlen=4096 * 128)
+    st, need = _ws_size(lib, big)
+    assert st == bd.LF_OK and need > 128 << 20
+    assert call(big) == bd.LF_EUNSUPPORTED
+    assert b"static scratch" in lib.lf_last_error()
+    # the headline shape fits
+    st, need = _ws_size(lib, _shape(batch=1, heads_q=32, heads_kv=8, seqlen=32768))
+    assert st == bd.LF_OK and need <= 128 << 20
