@@ -66,6 +66,16 @@ bool any_null(std::initializer_list<const void*> ptrs) {
     return false;
 }
 
+// true when a non-NULL pointer of the list is not a multiple of `a` bytes
+bool misaligned(std::initializer_list<const void*> ptrs, uintptr_t a) {
+    for (const void* p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) % a != 0) return true;
+    return false;
+}
+constexpr const char* kAlignMsg =
+    "misaligned pointer (element tensors and workspace: 16 bytes; other arrays: their element "
+    "size)";
+
 // A variable-length batch: shape->batch sequences, sequence b of
 // cu[b + 1] - cu[b] tokens (shape->seqlen is not used).  Checks every
 // sequence before anything is launched; fills one Problem per sequence.
@@ -131,6 +141,7 @@ lf_status lf_attn_fwd(const lf_shape* s, const void* q, const void* k, const voi
     if (st != LF_OK) return st;
     if (empty) return hip_status(hipSuccess);
     if (any_null({q, k, v, o, lse})) return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({q, k, v, o}, 16) || misaligned({lse}, 4)) return fail(LF_EINVAL, kAlignMsg);
     return hip_status(lf::launch_fwd(pb, q, k, v, o, lse, (hipStream_t)stream));
 }
 
@@ -152,6 +163,9 @@ lf_status lf_block_select_rule(const lf_shape* s, const void* o, const void* dou
     if (empty) return hip_status(hipSuccess);
     if (any_null({o, dout, D, mass, tau, block_w, kept_idx, kept_count}))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({o, dout}, 16) || misaligned({D, block_w, kept_idx, kept_count}, 4) ||
+        misaligned({mass, tau}, 8))
+        return fail(LF_EINVAL, kAlignMsg);
     return hip_status(lf::launch_select(pb, o, dout, rule, param, seed, D, mass, tau, block_w,
                                         kept_idx, kept_count, (hipStream_t)stream));
 }
@@ -187,6 +201,9 @@ lf_status lf_attn_bwd_phases(const lf_shape* s, const void* q, const void* k, co
     if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w}) ||
         ((phases & LF_BWD_DQ) && !dq) || ((phases & LF_BWD_DKDV) && (!dk || !dv)))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({q, k, v, dout, dq, dk, dv, workspace}, 16) ||
+        misaligned({lse, D, kept_idx, kept_count, block_w}, 4))
+        return fail(LF_EINVAL, kAlignMsg);
     if (phases & LF_BWD_DQ) {
         const size_t need = lf::bwd_workspace_bytes(pb);
         if (need > 0 && !workspace) return fail(LF_EINVAL, "workspace is NULL");
@@ -216,6 +233,9 @@ lf_status lf_attn_bwd_noalloc(const lf_shape* s, const void* q, const void* k, c
     if (empty) return hip_status(hipSuccess);
     if (any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv}))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({q, k, v, dout, dq, dk, dv}, 16) ||
+        misaligned({lse, D, kept_idx, kept_count, block_w}, 4))
+        return fail(LF_EINVAL, kAlignMsg);
     const size_t need = lf::bwd_workspace_bytes(pb), have = lf::static_scratch_bytes();
     if (need > have) {
         std::snprintf(g_err, sizeof(g_err),
@@ -239,6 +259,7 @@ lf_status lf_attn_fwd_varlen(const lf_shape* s, const int32_t* cu, const void* q
     if (st != LF_OK) return st;
     if (cu && s->batch > 0 && cu[s->batch] > 0 && any_null({q, k, v, o, lse}))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({q, k, v, o}, 16) || misaligned({lse}, 4)) return fail(LF_EINVAL, kAlignMsg);
     const size_t elt = s->dtype == LF_BF16 ? 2 : 4, d = (size_t)s->head_dim;
     for (const lf::Problem& pb : seqs) {
         if (pb.N == 0) continue;
@@ -268,6 +289,9 @@ lf_status lf_block_select_varlen(const lf_shape* s, const int32_t* cu, const voi
     }
     if (s->batch > 0 && any_null({o, dout, D, mass, tau, block_w, kept_idx, kept_count}))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({o, dout}, 16) || misaligned({D, block_w, kept_idx, kept_count}, 4) ||
+        misaligned({mass, tau}, 8))
+        return fail(LF_EINVAL, kAlignMsg);
     const size_t elt = s->dtype == LF_BF16 ? 2 : 4, d = (size_t)s->head_dim;
     size_t cb = 0;  // blocks of the sequences before this one
     for (const lf::Problem& pb : seqs) {
@@ -312,6 +336,9 @@ lf_status lf_attn_bwd_varlen(const lf_shape* s, const int32_t* cu, const void* q
     if (s->batch > 0 &&
         any_null({q, k, v, lse, dout, D, kept_idx, kept_count, block_w, dq, dk, dv}))
         return fail(LF_EINVAL, "NULL tensor pointer");
+    if (misaligned({q, k, v, dout, dq, dk, dv, workspace}, 16) ||
+        misaligned({lse, D, kept_idx, kept_count, block_w}, 4))
+        return fail(LF_EINVAL, kAlignMsg);
     size_t need = 0;
     for (const lf::Problem& pb : seqs)
         if (pb.N > 0) need = std::max(need, lf::bwd_workspace_bytes(pb));

@@ -84,42 +84,41 @@ __device__ __forceinline__ void map_bwd_block(int bid, int B, int Hkv, int& b, i
 // blocks in ascending order, and the 64-row sub-tiles of each block that reach
 // the workgroup's keys under the causal mask.  The walk position is uniform
 // (scalar registers); the kept list is read 64 entries at a time into one
-// vector register per wave (entry pos - cbase in lane pos - cbase), together
-// with log2 of each entry's weight, and looked up with v_readlane, so moving
-// to the next sub-tile costs no memory round trip.
+// vector register per wave (entry pos - cbase in lane pos - cbase) and looked
+// up with v_readlane, so moving to the next sub-tile costs no memory round
+// trip.  A head's count and first entries are requested together (one round
+// trip); the block weights are not part of the walk (each sub-tile's weight is
+// loaded with its rows).
 template <int BLK, bool CAUSAL>
 struct Walk {
     static_assert(kBN % BLK == 0 && BLK % kBM == 0, "key tiles start on block boundaries");
     const int32_t* kept_idx;
     const int32_t* kept_count;
-    const float* block_w;
     int Hq, nqb, G, b, g, k0, lane;
     int hg, cnt, pos, st, i, bh, cbase;
-    float lw;
     int vidx;    // kept_idx[bh][cbase + lane]  (or a large sentinel past cnt)
-    float vlw;   // log2(block_w[bh][vidx])
 
-    __device__ __forceinline__ void load_chunk(int c) {
-        cbase = __builtin_amdgcn_readfirstlane(c);
-        const int p = c + lane;
-        int idx = 0x7fffffff;
-        float w = 1.f;
-        if (p < cnt) {
-            idx = kept_idx[(size_t)bh * nqb + p];
-            if ((unsigned)idx < (unsigned)nqb) w = block_w[(size_t)bh * nqb + idx];
-        }
-        vidx = idx;
-        vlw = __log2f(w);
+    // entries c .. c + 63 of the current head's list (unmasked; clamped reads)
+    __device__ __forceinline__ int chunk_raw(int c) const {
+        return kept_idx[(size_t)bh * nqb + min(c + lane, nqb - 1)];
     }
-    __device__ __forceinline__ void load_head() {
+    __device__ __forceinline__ void set_chunk(int c, int raw) {
+        cbase = __builtin_amdgcn_readfirstlane(c);
+        vidx = c + lane < cnt ? raw : 0x7fffffff;
+    }
+    __device__ __forceinline__ void load_chunk(int c) { set_chunk(c, chunk_raw(c)); }
+    // the count and the first chunk of head hg are requested before either is
+    // used; returns with pos at the first kept block whose rows reach key k0
+    // (all of them when not causal)
+    __device__ __forceinline__ void load_head(int raw = -1, bool have_raw = false) {
         bh = b * Hq + g * G + hg;
+        if (!have_raw) raw = chunk_raw(0);
         cnt = __builtin_amdgcn_readfirstlane(min(max(kept_count[bh], 0), nqb));
         st = 0;
         pos = cnt;
-        // first kept block whose rows reach key k0 (all of them when not causal)
         const int first_block = CAUSAL ? k0 / BLK : 0;
         for (int c = 0; c < cnt; c += 64) {
-            load_chunk(c);
+            set_chunk(c, c == 0 ? raw : chunk_raw(c));
             const uint64_t m = __builtin_amdgcn_ballot_w64(vidx >= first_block);
             if (m) {
                 pos = __builtin_amdgcn_readfirstlane(c + (int)__builtin_ctzll(m));
@@ -146,14 +145,14 @@ struct Walk {
                 ++st;
                 continue;
             }
-            lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                               __builtin_bit_cast(int, vlw), pos - cbase));
             return true;
         }
     }
-    __device__ __forceinline__ bool first() {
+    // the first head's chunk 0 was requested by the caller (chunk_raw(0) with
+    // hg = 0 and bh set)
+    __device__ __forceinline__ bool first(int raw0) {
         hg = 0;
-        load_head();
+        load_head(raw0, true);
         return settle();
     }
     // Fast paths first: the next sub-tile of the same block, then the next
@@ -169,8 +168,6 @@ struct Walk {
                 pos += 1;
                 st = 0;
                 i = ni;
-                lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                   __builtin_bit_cast(int, vlw), np));
                 return true;
             }
         }
@@ -515,21 +512,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     const f32x16 zero16 = {};
     const TileOffsets<HD> off(lane);
 
-    bf16x8 kf[KS], vf[KS];
-    {
-        const size_t r = kvoff + (size_t)(key_ok ? key : 0) * HD;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = *reinterpret_cast<const bf16x8*>(k + r + 16 * ks + 8 * hf);
-            vf[ks] = *reinterpret_cast<const bf16x8*>(v + r + 16 * ks + 8 * hf);
-            if (!key_ok) { kf[ks] = bf16x8{}; vf[ks] = bf16x8{}; }
-        }
-    }
-
     Walk<BLK, CAUSAL> W;
     W.kept_idx = kept_idx;
     W.kept_count = kept_count;
-    W.block_w = block_w;
     W.lane = lane;
     W.Hq = Hq;
     W.nqb = nqb;
@@ -537,8 +522,27 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     W.b = b;
     W.g = g;
     W.k0 = k0;
+    W.hg = 0;
+    W.bh = b * Hq + g * G;
+    // the walk's first request (count and first kept entries of the group's
+    // first head) goes out before the K/V rows, so that waiting for it does
+    // not wait for them; keys past N read as zeros (buffer bounds)
+    const int raw0 = W.chunk_raw(0);
+    bf16x8 kf[KS], vf[KS];
+    {
+        const uint32_t kv_bytes = (uint32_t)N * HD * sizeof(bf16);
+        const auto rk = make_rsrc(k + kvoff, kv_bytes), rv = make_rsrc(v + kvoff, kv_bytes);
+        const int r = key * HD * (int)sizeof(bf16);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int o = r + (16 * ks + 8 * hf) * (int)sizeof(bf16);
+            kf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            vf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        }
+    }
+    const bool has_work = W.first(raw0);
 
-    float pld = 0.f;
+    float pld = 0.f, pw = 1.f;
     bool pld_ok = true;
     const uint32_t head_bytes = (uint32_t)N * HD * sizeof(bf16);
     // a sub-tile's Q and dO rows go straight to LDS; its LSE and D values to
@@ -553,11 +557,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
         const int row = qs0 + (tid & (kBM - 1));
         pld_ok = row < N;
         pld = (tid < kBM ? lse : Drow)[(size_t)bh * N + (pld_ok ? row : N - 1)];
+        pw = block_w[(size_t)bh * nqb + qs0 / BLK];
     };
     // LSE' = LSE log2 e - log2 w and -D (the start of the dP products); rows
     // past N get LSE' = +inf (P = 0) and D = 0
-    auto stage_rows = [&](float* sl, float* sn, float lw) __attribute__((always_inline)) {
-        if (tid < kBM) sl[tid] = pld_ok ? pld * kLog2e - lw : __builtin_inf();
+    auto stage_rows = [&](float* sl, float* sn) __attribute__((always_inline)) {
+        if (tid < kBM) sl[tid] = pld_ok ? pld * kLog2e - __log2f(pw) : __builtin_inf();
         else if (tid < 2 * kBM) sn[tid - kBM] = pld_ok ? -pld : 0.f;
     };
     // Zero packed P', dS' of the wave's rows (32 R + 8 (r >> 2) + 4 hf + (r & 3))
@@ -586,9 +591,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
         f32x16 acc[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16;
-        if (W.first()) {
+        if (has_work) {
             int cur_bh = W.bh, cur_q0 = W.q0();
-            float cur_lw = W.lw;
             fetch(cur_bh, cur_q0, sQ0, sO0);
             {   // the "previous" sub-tile of the first one: zero rows, zero
                 // exchanged operands, so its dV/dK products add exact zeros
@@ -599,7 +603,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
                 for (int c = tid; c < NW * 2 * 64; c += NW * 64) zx[c] = u32x4{};
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            stage_rows(sL[0], sN[0], cur_lw);
+            stage_rows(sL[0], sN[0]);
             __syncthreads();
 
             constexpr int NMF = 4 * DT;                 // dV or dK MFMAs per sub-tile
@@ -615,7 +619,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
                 // reload keeps the iteration free of branches)
                 const int nx_bh = more ? W.bh : cur_bh;
                 const int nx_q0 = more ? W.q0() : cur_q0;
-                const float nx_lw = more ? W.lw : cur_lw;
                 const int thr = !key_ok ? (1 << 30) : (CAUSAL ? key - cur_q0 - 4 * hf : -(1 << 30));
                 const bool wave_masked = __builtin_amdgcn_readfirstlane(
                     (int)(k0 + 32 * kg + 31 >= N || (CAUSAL && cur_q0 + 32 * R < k0 + 32 * kg + 31)));
@@ -706,12 +709,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
                     own[h] = R ? da[h] : pa[h];
                 }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                stage_rows(nl, nn, nx_lw);
+                stage_rows(nl, nn);
                 __syncthreads();
                 par ^= 1;
                 cur_bh = nx_bh;
                 cur_q0 = nx_q0;
-                cur_lw = nx_lw;
                 return more;
             };
             int last;
@@ -737,15 +739,44 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
                 }
             }
         }
-        bf16* out = R ? dk : dv;
-        const float sc = R ? scale : 1.f;
+        // The accumulators leave through LDS, so that each lane stores 16
+        // contiguous bytes: the role's 128 keys x HD go to two staging tiles
+        // (dV: sQ0, sO0; dK: sQ1, sO1; keys 64 t .. 64 t + 63 in tile t), in the
+        // swizzled layout of the walk's tiles, once every wave is done with them.
+        __syncthreads();
+        {
+            bf16* stg = R ? (kg < 2 ? sQ1 : sO1) : (kg < 2 ? sQ0 : sO0);
+            const float sc = R ? scale : 1.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kr = k0 + 32 * kg + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (kr < N) out[kvoff + (size_t)kr * HD + 32 * dt + l32] = to_bf16(acc[dt][r] * sc);
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * (kg & 1) + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    const int col = 32 * dt + l32;
+                    stg[row * HD + (((col >> 3) ^ swz<HD>(row)) << 3) + (col & 7)] =
+                        to_bf16(acc[dt][r] * sc);
+                }
+        }
+        __syncthreads();
+        {
+            constexpr int CPR = HD / 8;                   // 16-byte chunks per row
+            constexpr int NCH = 2 * kBM * CPR / 256;      // chunks per thread of the role
+            const bf16* t0 = R ? sQ1 : sQ0;
+            const bf16* t1 = R ? sO1 : sO0;
+            bf16* out = R ? dk : dv;
+            const int rt = tid & 255;
+#pragma unroll
+            for (int m = 0; m < NCH; ++m) {
+                const int c = rt + 256 * m;
+                const int t = c / (kBM * CPR), row = (c / CPR) % kBM, cc = c % CPR;
+                const bf16* tile = t ? t1 : t0;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(
+                    tile + row * HD + ((cc ^ swz<HD>(row)) << 3));
+                const int kr = k0 + kBM * t + row;
+                if (kr < N)
+                    *reinterpret_cast<u32x4*>(out + kvoff + (size_t)kr * HD + 8 * cc) = x;
             }
+        }
     };
     if (wave >= 4) walk(IntC<1>{});
     else walk(IntC<0>{});

@@ -41,6 +41,10 @@
  *     a static device array of the library (one per GPU, loaded with the
  *     library's kernels).  Work is enqueued on `stream` (a hipStream_t; NULL =
  *     the default stream) and the call returns without waiting for it.
+ *   - Alignment: the element tensors (Q, K, V, O, dO, dQ, dK, dV) and the
+ *     workspace start on a 16-byte boundary (the kernels move them in 16-byte
+ *     pieces); the other arrays on their element size (4 bytes; 8 for the
+ *     double-precision mass and tau).  A misaligned pointer is LF_EINVAL.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     failed check returns LF_EINVAL (malformed) or LF_EUNSUPPORTED (valid
  *     but outside what the kernels implement) and launches nothing.  A failed

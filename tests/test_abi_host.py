@@ -324,3 +324,22 @@ def test_noalloc_backward_checks_before_any_launch():
     # the headline shape fits
     st, need = _ws_size(lib, _shape(batch=1, heads_q=32, heads_kv=8, seqlen=32768))
     assert st == bd.LF_OK and need <= 128 << 20
+
+
+@pytest.mark.parametrize("addr", [0x1008, 0x1002])
+def test_misaligned_pointers_rejected_before_any_launch(addr):
+    # element tensors and the workspace move in 16-byte pieces: a pointer off a
+    # 16-byte boundary is refused on the host, whatever else is right
+    lib = bd.load(LIB)
+    mis = ctypes.c_void_p(addr)
+    shp = _shape()
+    assert _fwd(lib, shp, ptr=mis) == bd.LF_EINVAL
+    assert b"misaligned" in lib.lf_last_error()
+    assert _sel(lib, shp, 0.1, ptr=mis) == bd.LF_EINVAL
+    assert _bwd(lib, shp, ptr=mis) == bd.LF_EINVAL
+    assert _bwd(lib, shp, ws=mis) == bd.LF_EINVAL     # only the workspace is off
+    assert b"misaligned" in lib.lf_last_error()
+    assert lib.lf_attn_bwd_noalloc(ctypes.byref(shp), mis, mis, mis, mis, mis, mis, mis, mis, mis,
+                                   mis, mis, mis, NULL) == bd.LF_EINVAL
+    f, s, b, _, _ = _varlen(lib, _shape(batch=2, seqlen=0), [0, 100, 356], ptr=mis)
+    assert (f, s, b) == (bd.LF_EINVAL,) * 3
