@@ -413,28 +413,41 @@ def mfma_ceiling(reps, peak, n=16384):
     """The bf16 MFMA rate this GPU sustains on a plain large GEMM (the vendor
     library behind torch.matmul, N(0,1) operands), timed like the kernels.
     Sustained MFMA work lowers the clock below the 2.4 GHz of the published
-    peak, so this is the practical ceiling the kernels are compared with."""
+    peak, so this is the practical ceiling the kernels are compared with.  The
+    same GEMM on all-zero operands is timed too: the clock the chip holds
+    depends on the data the MFMAs switch, and random operands (like the
+    kernels' real inputs) hold it lowest."""
     import torch
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(0)
     a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
     b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
-    for _ in range(2):
-        c = a @ b
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        c = a @ b
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del a, b, c
+
+    def timed(x, y):
+        for _ in range(2):
+            c = x @ y
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = x @ y
+        e1.record()
+        torch.cuda.synchronize()
+        del c
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(a, b)
+    z = torch.zeros_like(a)
+    ms_zero = timed(z, z)
+    del a, b, z
     tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    tf_zero = 2.0 * n ** 3 / (ms_zero * 1e-3) / 1e12
     return dict(kind=f"torch.matmul bf16 {n}x{n}x{n}, N(0,1) operands (vendor GEMM)", reps=reps,
                 ms=round(ms, 4), achieved=round(tf, 2), unit="TFLOP/s",
-                frac_of_peak=round(tf / peak, 4))
+                frac_of_peak=round(tf / peak, 4),
+                zero_operands_tflops=round(tf_zero, 2),
+                zero_operands_frac_of_peak=round(tf_zero / peak, 4))
 
 
 def selection_rules_report(cfg, q, k, v, o, lse, do, ws, delta, kept_frac, steps):
