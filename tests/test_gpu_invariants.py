@@ -208,3 +208,20 @@ def test_concurrent_streams_share_no_state():
     for (_, outs), r in zip(jobs, ref):
         for a, b in zip(outs(), r):
             assert np.array_equal(a, b)
+
+
+def test_misaligned_tensor_refused_before_any_launch():
+    # a contiguous view two bytes into its storage: the library moves element
+    # tensors in 16-byte pieces, so it refuses the pointer and launches nothing
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, N, d = 1, 2, 1, 256, 64
+    n = B * Hq * N * d
+    base = torch.zeros(n + 8, dtype=torch.bfloat16, device=dev)
+    q_mis = base[1:1 + n].view(B, Hq, N, d)
+    assert q_mis.is_contiguous() and q_mis.data_ptr() % 16 == 2
+    k = torch.zeros((B, Hkv, N, d), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(bd.LazyFlashError, match="misaligned"):
+        bd.attn_fwd(q_mis, k, k, causal=True, block=64)
+    o, lse = bd.attn_fwd(q_mis.clone(), k, k, causal=True, block=64)  # aligned copy runs
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
