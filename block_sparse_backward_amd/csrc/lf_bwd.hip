@@ -107,12 +107,16 @@ struct Walk {
         vidx = c + lane < cnt ? raw : 0x7fffffff;
     }
     __device__ __forceinline__ void load_chunk(int c) { set_chunk(c, chunk_raw(c)); }
-    // the count and the first chunk of head hg are requested before either is
-    // used; returns with pos at the first kept block whose rows reach key k0
-    // (all of them when not causal)
-    __device__ __forceinline__ void load_head(int raw = -1, bool have_raw = false) {
+    // makes head h of the group current (its list is then requested with
+    // chunk_raw(0) and taken up by load_head)
+    __device__ __forceinline__ void begin_head(int h) {
+        hg = h;
         bh = b * Hq + g * G + hg;
-        if (!have_raw) raw = chunk_raw(0);
+    }
+    // `raw` = chunk_raw(0) of the current head, requested before its count is
+    // read, so the two round trips overlap; leaves pos at the first kept block
+    // whose rows reach key k0 (all of them when not causal)
+    __device__ __forceinline__ void load_head(int raw) {
         cnt = __builtin_amdgcn_readfirstlane(min(max(kept_count[bh], 0), nqb));
         st = 0;
         pos = cnt;
@@ -130,8 +134,9 @@ struct Walk {
     __device__ __forceinline__ bool settle() {
         while (true) {
             if (pos >= cnt) {
-                if (++hg >= G) return false;
-                load_head();
+                if (hg + 1 >= G) return false;
+                begin_head(hg + 1);
+                load_head(chunk_raw(0));
                 continue;
             }
             if (pos - cbase >= 64) load_chunk(pos & ~63);
@@ -148,11 +153,10 @@ struct Walk {
             return true;
         }
     }
-    // the first head's chunk 0 was requested by the caller (chunk_raw(0) with
-    // hg = 0 and bh set)
+    // the caller made head 0 current (begin_head(0)) and passes its
+    // chunk_raw(0), requested ahead of other loads
     __device__ __forceinline__ bool first(int raw0) {
-        hg = 0;
-        load_head(raw0, true);
+        load_head(raw0);
         return settle();
     }
     // Fast paths first: the next sub-tile of the same block, then the next
@@ -522,8 +526,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(
     W.b = b;
     W.g = g;
     W.k0 = k0;
-    W.hg = 0;
-    W.bh = b * Hq + g * G;
+    W.begin_head(0);
     // the walk's first request (count and first kept entries of the group's
     // first head) goes out before the K/V rows, so that waiting for it does
     // not wait for them; keys past N read as zeros (buffer bounds)
