@@ -339,9 +339,10 @@ def main():
 def config_rows(cfg, steps, peak):
     """One compact row per delta of workload `cfg`: select + backward (the
     library's one call) per microbatch, effective dense-equivalent TFLOP/s,
-    the kept fractions, and the dK/dV walk alone (timed in a second pass over
+    the kept fractions, the dK/dV walk alone (timed in a second pass over
     the same seeds) with its roofline fraction on its algorithmic work
-    (0.8 F_kept; bf16 only, the fp32 path does not use the matrix cores)."""
+    (0.8 F_kept; bf16 only, the fp32 path does not use the matrix cores), and
+    the speedup over the same kernels at delta = 0."""
     import numpy as np
     import torch
 
@@ -404,6 +405,28 @@ def config_rows(cfg, steps, peak):
             dkdv_tf = float(0.8 * flops.sum() / (t[:, 1].sum() * 1e-3) / 1e12)
             row["dkdv_roofline_frac"] = round(dkdv_tf / peak, 4)
         rows.append(row)
+    # the same kernels at delta = 0 (every block kept, weight 1): the dense
+    # reference each row's speedup is taken against
+    dense = [r["attn_bwd_ms"] for r in rows if r["delta"] == 0.0]
+    if dense:
+        dense_ms = dense[0]
+    else:
+        log(f"[bench] config {cfg.name} delta=0 (dense reference)")
+        sel = bd.select_outputs(cfg.B, cfg.Hq, cfg.N, cfg.block, dev)
+        select(0.0, 30_000, sel)
+        bd.attn_bwd(q, k, v, lse, do, sel, **common)  # warm-up
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for seed, e in enumerate(ev):
+            e[0].record(stream)
+            select(0.0, seed, sel)
+            bd.attn_bwd(q, k, v, lse, do, sel, **common)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    for r in rows:
+        r["dense_attn_bwd_ms"] = round(dense_ms, 4)
+        r["speedup_vs_own_dense"] = round(dense_ms / r["attn_bwd_ms"], 3)
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return rows
