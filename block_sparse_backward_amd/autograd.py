@@ -35,11 +35,19 @@ def draw_seed(step, layer=0, base=0):
     return (base << (_STEP_BITS + _LAYER_BITS)) | (step << _LAYER_BITS) | layer
 
 
+def _dense(t):
+    """t contiguous and on a 16-byte boundary (the library moves element
+    tensors in 16-byte pieces and refuses other pointers): a copy only when
+    t is neither."""
+    t = t.contiguous()
+    return t if t.data_ptr() % 16 == 0 else t.clone()
+
+
 class LazyFlashAttention(torch.autograd.Function):
     """o = attention(q, k, v); backward = block selection + sparse backward.
 
     q [B, Hq, N, d], k and v [B, Hkv, N, d]: GPU tensors, bfloat16 or float32
-    (made contiguous here).  delta in [0, 1) is the budget on the discarded
+    (copied here when not contiguous or not on a 16-byte boundary).  delta in [0, 1) is the budget on the discarded
     gradient mass (0 keeps every block: the exact dense gradient); seed keys
     the draw.  If `stats` is a dict, the backward stores in it the selection's
     device tensors (mass, tau, block_w, kept_idx, kept_count) without waiting
@@ -48,7 +56,7 @@ class LazyFlashAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, delta, seed, causal, scale, block, stats, rule=binding.SELECT_BUDGET):
-        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        q, k, v = _dense(q), _dense(k), _dense(v)
         o, lse = binding.attn_fwd(q, k, v, causal=causal, scale=scale, block=block)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.cfg = (float(delta), int(seed), bool(causal), scale, int(block), stats, int(rule))
@@ -58,7 +66,7 @@ class LazyFlashAttention(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         delta, seed, causal, scale, block, stats, rule = ctx.cfg
-        do = do.to(q.dtype).contiguous()
+        do = _dense(do.to(q.dtype))
         sel = binding.block_select(o, do, delta, seed, block=block, causal=causal, scale=scale,
                                    heads_kv=k.shape[1], rule=rule)
         dq, dk, dv = binding.attn_bwd(q, k, v, lse, do, sel, block=block, causal=causal,

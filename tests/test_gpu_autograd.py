@@ -78,6 +78,31 @@ def test_autograd_accepts_views_and_accumulates_into_leaves():
         assert max_abs_rel(host(t.grad.transpose(1, 2)), r) <= TOL["bf16"]
 
 
+def test_autograd_accepts_misaligned_contiguous_inputs():
+    # contiguous views two bytes into their storage: the library refuses such
+    # pointers, so the wrapper copies them; the result is the aligned one's
+    cfg = Config("ag7", 1, 4, 2, 256, 64, "bf16", True, 64, 1.0)
+    inp = make_inputs(cfg, 0)
+    dev = torch.device("cuda:0")
+
+    def offset_copy(t):
+        base = torch.zeros(t.numel() + 8, dtype=t.dtype, device=dev)
+        view = base[1:1 + t.numel()].view(t.shape)
+        view.copy_(t.to(dev))
+        assert view.is_contiguous() and view.data_ptr() % 16 != 0
+        return view
+
+    grads = []
+    for make in (lambda t: t.to(dev).clone(), offset_copy):
+        leaves = [make(inp[n]).requires_grad_(True) for n in ("q", "k", "v")]
+        o = lazyflash_attention(*leaves, 0.1, 3, causal=True, scale=cfg.scale, block=cfg.block)
+        o.backward(offset_copy(inp["dout"]) if make is offset_copy else inp["dout"].to(dev))
+        torch.cuda.synchronize()
+        grads.append([o.detach()] + [t.grad for t in leaves])
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)
+
+
 def test_new_seed_redraws_and_same_seed_repeats():
     cfg = Config("ag6", 1, 4, 2, 1024, 128, "bf16", True, 128, 1.0)
     inp = make_inputs(cfg, 0)
