@@ -285,7 +285,7 @@ const char* lf_last_error(void);
 /* ABI version of this header, for run-time checks by bindings. */
 int32_t lf_abi_version(void);
 
-#define LF_ABI_VERSION 7  /* 7: lf_attn_bwd_noalloc; 6: D on kept rows only */
+#define LF_ABI_VERSION 8  /* 8: misaligned pointers refused; 7: lf_attn_bwd_noalloc; 6: D on kept rows only */
 
 #ifdef __cplusplus
 }
