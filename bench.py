@@ -267,6 +267,35 @@ def main():
         ceiling = mfma_ceiling(args.ceiling_reps, peak)
         ceiling["dkdv_vs_ceiling"] = round(achieved / ceiling["achieved"], 4)
         ceiling["fwd_vs_ceiling"] = round(others["fwd"]["achieved"] / ceiling["achieved"], 4)
+        # context, not a result: the dK/dV walk on one selection, with the real
+        # Q, K, V, dO and with all-zero ones (same kept blocks, same work): the
+        # clock the chip holds depends on the data the MFMAs switch
+        sel = bd.block_select(o, do, main_delta, 0, block=cfg.block, causal=cfg.causal,
+                              scale=cfg.scale, heads_kv=cfg.Hkv)
+        zeros = [torch.zeros_like(t) for t in (q, k, v, do)]
+        kw = dict(block=cfg.block, causal=cfg.causal, scale=cfg.scale, out=(dq, dk, dv),
+                  workspace=ws, phases=bd.BWD_DKDV)
+
+        def dkdv_ms(qq, kk, vv, dd):
+            bd.attn_bwd(qq, kk, vv, lse, dd, sel, **kw)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(args.ceiling_reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                bd.attn_bwd(qq, kk, vv, lse, dd, sel, **kw)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts))
+        real_ms = dkdv_ms(q, k, v, do)
+        zero_ms = dkdv_ms(*zeros)
+        del zeros
+        ceiling["dkdv_same_selection"] = dict(
+            real_operands_ms=round(real_ms, 4), zero_operands_ms=round(zero_ms, 4),
+            zero_over_real_speed=round(real_ms / zero_ms, 3),
+            note="the dK/dV walk alone, one selection, median of the reps; zero operands are "
+                 "context for the clock's data dependence, never a result")
 
     cpu = None
     if not args.no_cpu_baseline:
