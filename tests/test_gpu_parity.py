@@ -46,6 +46,14 @@ SMALL = {
     "bf16_xcd_B2_Hkv4": (Config("x1", 2, 8, 4, 640, 128, "bf16", True, 128, 2.0,
                                 boost_frac=0.1, boost=20.0), 0.1),
     "bf16_xcd_B3_Hkv8_d64_b64": (Config("x2", 3, 8, 8, 384, 64, "bf16", True, 64, 1.5), 0.1),
+    # odd group sizes: 3 and 5 query heads per kv head (the walks over a
+    # group's heads and the head-to-group maps)
+    "bf16_gqa3_d128_b64": (Config("g3", 1, 6, 2, 448, 128, "bf16", True, 64, 1.5,
+                                  boost_frac=0.2, boost=20.0), 0.1),
+    "bf16_gqa5_noncausal_d64_b128_ragged": (Config("g5", 2, 5, 1, 333, 64, "bf16", False, 128,
+                                                   1.0), 0.2),
+    "bf16_gqa3_B2_Hkv4_d128_b128_ragged": (Config("g3x", 2, 12, 4, 700, 128, "bf16", True, 128,
+                                                  2.0), 0.1),
 }
 
 
